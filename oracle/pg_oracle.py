@@ -1,0 +1,454 @@
+"""fp64 CPU oracle for packed shared-prefix causal attention.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The HIP library never calls it and
+shares no code with it; the two meet only through the seeded inputs of the
+``workloads`` package.
+
+What is computed, and where the pages fix it
+--------------------------------------------
+"Preference Packing: Efficient Preference Optimization for LLMs" (core idea,
+technical framework): samples that share a prompt are packed as the prompt once
+followed by each response; prompt attention is computed once and reused for
+every response, and the model itself is unchanged (key innovation).
+The verl ``prefix_grouper_utils.py`` page (section 1, building position ids,
+and the prefix-sharing diagram) fixes that every response continues the
+prefix independently and that its position ids restart at the prefix length.
+
+Hence the packed result has a plain definition: every packed row equals the
+row of textbook causal attention over the unpacked sequence prefix || response
+it belongs to. ``attention`` is that definition written out. ``attention_masked``
+is the packed form with an explicit key set per token, ``attention_dense`` the
+same with a dense T x T mask; tests tie all three together.
+
+Readings where the pages are silent (each listed in the design doc):
+  * RoPE is never defined on the pages: rotate-half convention on Q and K,
+    omega_i = theta^(-2i/d), i < d/2.
+  * softmax scale is an input (1/sqrt(d) in the workloads).
+  * GQA: query head h reads KV head h // (Hq / Hkv).
+  * lse is the natural log of the sum of exp of the *scaled* scores.
+  * zero-length suffixes occupy no tokens; P = 0 and n = 0 are legal.
+
+Every function is pinned by a ``-m "not gpu"`` test against something other
+than itself (hand-derived values, closed forms, a library routine, brute
+force); the pins are listed beside each function.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Sequence, Tuple
+
+import numpy as np
+
+# ------------------------------------------------------------------ layout --
+
+
+def layout(prefix_lens: Sequence[int], suffix_counts: Sequence[int],
+           suffix_lens: Sequence[int]) -> Dict[str, np.ndarray]:
+    """Token layout of the packed batch.
+
+    "Preference Packing" (technical framework, step 2): each group is stored as
+    its prompt once, then each of its responses. Groups and responses keep
+    input order (reading). Segments are listed per group as
+    [prefix, suffix_1, ..., suffix_n]; zero-length ones are kept in the list
+    and occupy no tokens (verl page, section 1: empty suffixes are skipped).
+
+    Per token t: g0 = first token of its group, pe = end of its group's prefix,
+    ss = start of its own segment (the group start for prefix tokens).
+
+    Pinned by: hand-derived offsets of the tiny workload (tests/golden).
+    """
+    P = [int(x) for x in prefix_lens]
+    n = [int(x) for x in suffix_counts]
+    S = [int(x) for x in suffix_lens]
+    if len(P) != len(n) or sum(n) != len(S):
+        raise ValueError("inconsistent lengths")
+    if min(P + n + S + [0]) < 0:
+        raise ValueError("negative length")
+    group_off = [0]
+    seg_off = [0]
+    g0: List[int] = []
+    pe: List[int] = []
+    ss: List[int] = []
+    k = 0
+    for g in range(len(P)):
+        start = group_off[-1]
+        pend = start + P[g]
+        seg_off.append(pend)
+        for t in range(start, pend):
+            g0.append(start)
+            pe.append(pend)
+            ss.append(start)
+        cur = pend
+        for _ in range(n[g]):
+            s_len = S[k]
+            k += 1
+            for t in range(cur, cur + s_len):
+                g0.append(start)
+                pe.append(pend)
+                ss.append(cur)
+            cur += s_len
+            seg_off.append(cur)
+        group_off.append(cur)
+    return {
+        "prefix_lens": np.asarray(P, dtype=np.int64),
+        "suffix_counts": np.asarray(n, dtype=np.int64),
+        "suffix_lens": np.asarray(S, dtype=np.int64),
+        "group_off": np.asarray(group_off, dtype=np.int64),
+        "seg_off": np.asarray(seg_off, dtype=np.int64),
+        "g0": np.asarray(g0, dtype=np.int64),
+        "pe": np.asarray(pe, dtype=np.int64),
+        "ss": np.asarray(ss, dtype=np.int64),
+        "total_tokens": group_off[-1],
+    }
+
+
+def sequences(lay) -> Iterable[Tuple[int, int, int, int]]:
+    """The unpacked sequences: (group, prefix start, prefix len, suffix span).
+
+    Yields (g, p0, P, (s0, s1)) per suffix; a group with no suffix yields once
+    with an empty suffix span, so its prefix still forms a sequence.
+    """
+    k = 0
+    for g in range(len(lay["prefix_lens"])):
+        p0 = int(lay["group_off"][g])
+        P = int(lay["prefix_lens"][g])
+        cur = p0 + P
+        n = int(lay["suffix_counts"][g])
+        if n == 0:
+            yield g, p0, P, (cur, cur)
+        for _ in range(n):
+            s = int(lay["suffix_lens"][k])
+            k += 1
+            yield g, p0, P, (cur, cur + s)
+            cur += s
+
+
+# --------------------------------------------------------------- positions --
+
+
+def positions(lay) -> np.ndarray:
+    """int64 position id per packed token.
+
+    verl page, section 1 (building position ids): within a group the prompt
+    takes 0..P-1; every non-empty response takes P..P+S-1, written right after
+    the previous one; empty responses consume nothing. Written here as that
+    loop over groups and responses, on the unpadded packed row.
+
+    Pinned by: hand-derived ids of the tiny workload; equality with
+    arange(P+S) of each unpacked sequence.
+    """
+    T = int(lay["total_tokens"])
+    pos = np.zeros(T, dtype=np.int64)
+    k = 0
+    for g in range(len(lay["prefix_lens"])):
+        base = int(lay["group_off"][g])
+        P = int(lay["prefix_lens"][g])
+        pos[base:base + P] = np.arange(P)
+        cur = base + P
+        for _ in range(int(lay["suffix_counts"][g])):
+            s = int(lay["suffix_lens"][k])
+            k += 1
+            if s > 0:
+                pos[cur:cur + s] = np.arange(P, P + s)
+                cur += s
+    return pos
+
+
+# -------------------------------------------------------------------- rope --
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary embedding (rotate-half convention) in fp64.
+
+    The pages never define RoPE; they only fix the positions it is applied at
+    (verl page, section 1). Reading: for i < d/2, omega_i = theta^(-2i/d),
+    phi = pos * omega_i, and the pair (x_i, x_{i+d/2}) is rotated by phi.
+
+    x: [T, H, d] (any float dtype); pos: int [T]. Returns fp64 [T, H, d].
+    Pinned by: complex-multiplication form, pos = 0 identity, pair norms,
+    dependence of <R(a)q, R(b)k> on b - a only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    omega = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    phi = np.asarray(pos, dtype=np.float64)[:, None] * omega[None, :]   # [T, d/2]
+    c = np.cos(phi)[:, None, :]
+    s = np.sin(phi)[:, None, :]
+    lo = x[..., :half]
+    hi = x[..., half:]
+    out = np.empty_like(x)
+    out[..., :half] = lo * c - hi * s
+    out[..., half:] = hi * c + lo * s
+    return out
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of fp64 input, returned as fp64.
+
+    bf16 keeps 8 significant bits; x = m * 2^e with 0.5 <= |m| < 1, so the
+    rounded value is rint(m * 2^8) * 2^(e - 8) (rint rounds ties to even).
+    Valid for normal numbers, which is all the workloads produce.
+    Pinned by: tie cases 1 + 2^-8 -> 1 and 1 + 3*2^-8 -> 1 + 2^-6.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def storage_round(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values to the storage dtype of a workload (fp64 out)."""
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------- attention --
+
+
+def _kv_head(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """GQA reading: consecutive query heads share a KV head."""
+    return h // (num_q_heads // num_kv_heads)
+
+
+def _causal_rows(q_rows: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
+                 row_index: np.ndarray, scale: float):
+    """Textbook causal softmax attention for selected rows of one sequence.
+
+    Row i of the sequence attends keys 0..i. q_rows: [R, d] (rows with
+    sequence indices ``row_index``), k_seq/v_seq: [L, d]. Returns (o [R, d],
+    lse [R]) with lse = max + ln(sum exp(s - max)) of the scaled scores.
+    """
+    s = scale * (q_rows @ k_seq.T)                               # [R, L]
+    cols = np.arange(k_seq.shape[0])[None, :]
+    s = np.where(cols <= row_index[:, None], s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ v_seq) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+def attention(q, k, v, lay, scale: float, num_q_heads: int, num_kv_heads: int,
+              row_chunk: int = 1024):
+    """Packed attention output by its definition: causal attention of each
+    unpacked sequence.
+
+    "Preference Packing" (core idea) and the verl prefix-sharing diagram: the
+    prompt's attention is computed once and each response continues it, as if
+    prompt || response were its own sequence. So prefix rows are the causal
+    attention of the prefix alone (they cannot see any suffix), and the rows of
+    suffix k are the suffix rows of causal attention over prefix || suffix_k.
+
+    q: [T, Hq, d], k/v: [T, Hkv, d] (any float dtype; computed in fp64).
+    Returns o fp64 [T, Hq, d] and lse fp64 [Hq, T].
+    Pinned by: equality with ``attention_masked`` and ``attention_dense`` and
+    with torch's float64 SDPA (library routine); special cases (first token,
+    constant V, identical keys, n = 1, P = 0, GQA vs repeated MHA).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, d = q.shape
+    o = np.zeros((T, Hq, d), dtype=np.float64)
+    lse = np.zeros((Hq, T), dtype=np.float64)
+    done_prefix = set()
+    for g, p0, P, (s0, s1) in sequences(lay):
+        tok = np.concatenate([np.arange(p0, p0 + P), np.arange(s0, s1)])
+        todo = [] if g in done_prefix else list(range(P))
+        todo += list(range(P, len(tok)))
+        done_prefix.add(g)
+        if not todo:
+            continue
+        rows = np.asarray(todo)
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, num_kv_heads)
+            ks = k[tok, hk]
+            vs = v[tok, hk]
+            for c0 in range(0, len(rows), row_chunk):
+                r = rows[c0:c0 + row_chunk]
+                oo, ll = _causal_rows(q[tok[r], h], ks, vs, r, scale)
+                o[tok[r], h] = oo
+                lse[h, tok[r]] = ll
+    return o, lse
+
+
+def allowed_keys(lay, t: int) -> np.ndarray:
+    """Key set K(t) of packed token t (reading of the mask, never written as a
+    formula on the pages): keys of its own group up to itself, except keys of a
+    sibling response. A prefix token sees its prefix causally; a response token
+    sees the whole prefix and its own response causally.
+
+    K(t) = { j : g0 <= j <= t and (j < pe or j >= ss) }.
+    Pinned by: equality of ``attention_masked`` with ``attention``.
+    """
+    g0, pe, ss = int(lay["g0"][t]), int(lay["pe"][t]), int(lay["ss"][t])
+    j = np.arange(g0, t + 1)
+    return j[(j < pe) | (j >= ss)]
+
+
+def attention_masked(q, k, v, lay, scale: float, num_q_heads: int,
+                     num_kv_heads: int):
+    """Packed attention over the packed row with the key set K(t) per token.
+
+    This is the form a packed kernel evaluates (one pass over the packed row,
+    PackInfer abstract: attention built directly over packed query-key
+    regions). Returns (o [T, Hq, d], lse [Hq, T]) in fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, d = q.shape
+    o = np.zeros((T, Hq, d))
+    lse = np.zeros((Hq, T))
+    for t in range(T):
+        keys = allowed_keys(lay, t)
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, num_kv_heads)
+            s = scale * (k[keys, hk] @ q[t, h])
+            m = s.max()
+            p = np.exp(s - m)
+            o[t, h] = (p @ v[keys, hk]) / p.sum()
+            lse[h, t] = m + math.log(p.sum())
+    return o, lse
+
+
+def segment_ids(lay) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Per token: group id, segment id (0 = prefix, k = suffix k), and a flag
+    for prefix tokens. Used only by the dense brute-force form."""
+    T = int(lay["total_tokens"])
+    grp = np.zeros(T, dtype=np.int64)
+    seg = np.zeros(T, dtype=np.int64)
+    k = 0
+    for g in range(len(lay["prefix_lens"])):
+        a, b = int(lay["group_off"][g]), int(lay["group_off"][g + 1])
+        grp[a:b] = g
+        cur = a + int(lay["prefix_lens"][g])
+        for j in range(int(lay["suffix_counts"][g])):
+            s = int(lay["suffix_lens"][k])
+            k += 1
+            seg[cur:cur + s] = j + 1
+            cur += s
+    return grp, seg, seg == 0
+
+
+def dense_mask(lay) -> np.ndarray:
+    """Dense T x T boolean mask from segment ids:
+    M[i, j] = same group and j <= i and (j is a prefix token or same segment).
+    """
+    grp, seg, is_pre = segment_ids(lay)
+    T = grp.shape[0]
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    return (grp[:, None] == grp[None, :]) & (j <= i) & (is_pre[None, :] | (seg[:, None] == seg[None, :]))
+
+
+def attention_dense(q, k, v, lay, scale: float, num_q_heads: int,
+                    num_kv_heads: int):
+    """Brute force: one softmax per head over all T keys with the dense mask.
+    For tiny inputs only (T <= a few hundred)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, d = q.shape
+    M = dense_mask(lay)
+    o = np.zeros((T, Hq, d))
+    lse = np.zeros((Hq, T))
+    for h in range(Hq):
+        hk = _kv_head(h, Hq, num_kv_heads)
+        s = np.where(M, scale * (q[:, h] @ k[:, hk].T), -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        l = p.sum(axis=1, keepdims=True)
+        o[:, h] = (p @ v[:, hk]) / l
+        lse[h] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def attention_rows(q, k, v, lay, scale: float, num_q_heads: int,
+                   num_kv_heads: int, tokens: Sequence[int], heads: Sequence[int]):
+    """Selected outputs by the definition, one (token, head) at a time.
+
+    For a prefix token at prefix index i: causal attention over prefix[0..i].
+    For a token at index i of suffix k: attention over the whole prefix and
+    suffix_k[0..i] (its unpacked sequence, causal). Returns o [n, d], lse [n]
+    for the pairs zip(tokens, heads). Cheap enough for full-size workloads.
+    """
+    T, Hq, d = q.shape
+    bounds = {}
+    for g, p0, P, (s0, s1) in sequences(lay):
+        for t in range(s0, s1):
+            bounds[t] = (p0, P, s0)
+    out_o = np.zeros((len(tokens), d))
+    out_l = np.zeros(len(tokens))
+    for n, (t, h) in enumerate(zip(tokens, heads)):
+        t, h = int(t), int(h)
+        hk = _kv_head(h, Hq, num_kv_heads)
+        if t in bounds:
+            p0, P, s0 = bounds[t]
+            keys = np.concatenate([np.arange(p0, p0 + P), np.arange(s0, t + 1)])
+        else:  # prefix token
+            g0 = int(lay["g0"][t])
+            keys = np.arange(g0, t + 1)
+        qq = np.asarray(q[t, h], dtype=np.float64)
+        kk = np.asarray(k[keys, hk], dtype=np.float64)
+        vv = np.asarray(v[keys, hk], dtype=np.float64)
+        s = scale * (kk @ qq)
+        m = s.max()
+        p = np.exp(s - m)
+        out_o[n] = (p @ vv) / p.sum()
+        out_l[n] = m + math.log(p.sum())
+    return out_o, out_l
+
+
+# ---------------------------------------------------------- FLOP accounting --
+
+
+def useful_pairs(lay) -> int:
+    """Number of allowed (query, key) pairs of the packed layout (per head).
+
+    Per group: P(P+1)/2 for the prompt plus S*P + S(S+1)/2 per response.
+    Pinned by: count of the dense mask; hand-derived 217 for the tiny workload.
+    """
+    total = 0
+    k = 0
+    for g in range(len(lay["prefix_lens"])):
+        P = int(lay["prefix_lens"][g])
+        total += P * (P + 1) // 2
+        for _ in range(int(lay["suffix_counts"][g])):
+            S = int(lay["suffix_lens"][k])
+            k += 1
+            total += S * P + S * (S + 1) // 2
+    return total
+
+
+def unpacked_pairs(lay) -> int:
+    """Pairs of causal attention over every unpacked sequence (the work that
+    preference packing removes is the repeated prompt triangle)."""
+    total = 0
+    for g, p0, P, (s0, s1) in sequences(lay):
+        L = P + (s1 - s0)
+        total += L * (L + 1) // 2
+    return total
+
+
+def useful_flop(lay, num_q_heads: int, head_dim: int) -> int:
+    """Useful FLOP: QK^T and PV multiply-adds over allowed pairs only."""
+    return 4 * head_dim * num_q_heads * useful_pairs(lay)
+
+
+# -------------------------------------------------------------- pipeline ----
+
+
+def pipeline(q, k, v, lay, theta: float, scale: float, num_q_heads: int,
+             num_kv_heads: int, dtype: str):
+    """positions -> RoPE (fp64, then rounded to the storage dtype, as the
+    RoPE step hands its result over in that dtype) -> attention."""
+    pos = positions(lay)
+    qr = storage_round(rope(q, pos, theta), dtype)
+    kr = storage_round(rope(k, pos, theta), dtype)
+    o, lse = attention(qr, kr, v, lay, scale, num_q_heads, num_kv_heads)
+    return pos, qr, kr, o, lse

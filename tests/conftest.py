@@ -1,0 +1,26 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def read_golden(name):
+    """Parse a ``key: values`` fixture under tests/golden (comments start with #)."""
+    out = {}
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            out[key.strip()] = [int(x) for x in val.split()]
+    return out
