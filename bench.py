@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed shared-prefix attention path on one MI355X.
+
+One step = the whole hot path over one batch already resident in HBM:
+  pg_build_layout (host builder + upload) -> pg_position_ids -> pg_rope (Q, K)
+  -> pg_attn_fwd (O, lse).
+Default workload: GRPO-style bf16, 16 prompts x 8 responses, 32/8 heads,
+d = 128 (the configuration the useful-TFLOP/s target is quoted on).
+
+Prints ONE JSON line. `value` = useful attention FLOP per step / step time
+(useful FLOP = 4 * d * Hq * allowed query-key pairs of the packed layout).
+`roofline` is for pg_attn_fwd alone, timed with HIP events on its stream.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+KERNEL_SOURCES = ["shared_prefix_packed_amd/csrc/pg_attn_mfma.hip",
+                  "shared_prefix_packed_amd/csrc/pg_internal.h",
+                  "shared_prefix_packed_amd/csrc/pg_layout.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per attention launch from committed rocprofv3 counters, or
+    None when they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(workload)
+    if not r or r.get("kernel_hash") != kernel_source_hash():
+        return None
+    return r.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, qkv, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
+    whole groups, one query head at a time (group-major), until the time
+    budget is spent. Reports useful FLOP/s of the sample."""
+    import numpy as np
+    from oracle import pg_oracle as O
+    from workloads import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    r = w.num_q_heads // w.num_kv_heads
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    conv = (lambda x: bf16_bits_to_f32(x)) if w.dtype == "bf16" else (lambda x: x)
+    t0 = time.perf_counter()
+    units = 0
+    flop = 0
+    groups = set()
+    soff = 0
+    for g in range(w.num_groups):
+        n = int(w.suffix_counts[g])
+        sub = O.layout(w.prefix_lens[g:g + 1], w.suffix_counts[g:g + 1],
+                       w.suffix_lens[soff:soff + n])
+        soff += n
+        a, b = int(lay["group_off"][g]), int(lay["group_off"][g + 1])
+        if b == a:
+            continue
+        for h in range(w.num_q_heads):
+            hk = h // r
+            q = conv(qkv["q"][a:b, h:h + 1])
+            k = conv(qkv["k"][a:b, hk:hk + 1])
+            v = conv(qkv["v"][a:b, hk:hk + 1])
+            O.attention(q, k, v, sub, w.softmax_scale, 1, 1)
+            units += 1
+            groups.add(g)
+            flop += 4 * w.head_dim * O.useful_pairs(sub)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle on {units} (group, query head) units from groups "
+                   f"{sorted(groups)} of {w.name}: {flop / 1e9:.1f} useful GFLOP in {dt:.1f} s; "
+                   f"BLAS threads={threads}, host cpus={os.cpu_count()}"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="workload index 0..4 (default 2: GRPO)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-unpacked", action="store_true", help="skip the unpacked-layout baseline")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(groups shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import shared_prefix_packed_amd as pg
+    from shared_prefix_packed_amd.baseline import unpacked_workload
+    from workloads import draw_qkv, make_workload, sha256
+
+    pg.load()   # fails loudly without the built library
+    w = make_workload(args.workload)
+    print(f"[bench] workload {w.name}: T={w.total_tokens} G={w.num_groups}", file=sys.stderr, flush=True)
+    qkv = draw_qkv(w)
+    dt_torch = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v = dev(qkv["q"]), dev(qkv["k"]), dev(qkv["v"])
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    stream = torch.cuda.current_stream()
+    qr = torch.empty_like(q)
+    kr = torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    pos = torch.empty(T, dtype=torch.int64, device="cuda")
+
+    def build():
+        return pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, Hq, Hkv, d,
+                                  w.rope_theta, stream=stream)
+
+    info = build()
+    summ = info.summary()
+    useful_flop = 4 * d * Hq * int(summ.useful_pairs)
+    info.close()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    attn_ms, rope_ms, pos_ms, layout_ms = [], [], [], []
+
+    def step(record):
+        t_host = time.perf_counter()
+        L = build()
+        t_host = time.perf_counter() - t_host
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record(stream)
+        pg.pg_position_ids(L, pos=pos, stream=stream)
+        e1.record(stream)
+        pg.pg_rope(L, pos, q, k, q_out=qr, k_out=kr, stream=stream)
+        e2.record(stream)
+        pg.pg_attn_fwd(L, qr, kr, v, w.softmax_scale, o=o, lse=lse, stream=stream)
+        e3.record(stream)
+        L.close()
+        if record:
+            layout_ms.append(t_host * 1e3)
+            return (e0, e1, e2, e3)
+        return None
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e0, e1, e2, e3 in events:
+        pos_ms.append(e0.elapsed_time(e1))
+        rope_ms.append(e1.elapsed_time(e2))
+        attn_ms.append(e2.elapsed_time(e3))
+    ms_per_step = wall * 1e3 / args.steps
+    attn_avg = float(np.mean(attn_ms))
+    attn_tflops = useful_flop / (attn_avg * 1e-3) / 1e12
+    value = useful_flop / (ms_per_step * 1e-3) / 1e12
+
+    # unpacked baseline (same kernel, prefix duplicated per response)
+    speedup = None
+    unpacked_ms = None
+    if not args.no_unpacked:
+        un = unpacked_workload(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+        idx = torch.from_numpy(un.gather).cuda()
+        qu, ku, vu = qr[idx].contiguous(), kr[idx].contiguous(), v[idx].contiguous()
+        Lu = pg.pg_build_layout(un.prefix_lens, un.suffix_counts, un.suffix_lens, Hq, Hkv, d,
+                                w.rope_theta, stream=stream)
+        ou = torch.empty_like(qu)
+        lu = torch.empty((Hq, qu.shape[0]), dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            pg.pg_attn_fwd(Lu, qu, ku, vu, w.softmax_scale, o=ou, lse=lu, stream=stream)
+        ts = []
+        for _ in range(max(3, args.steps // 2)):
+            a_, b_ = ev(), ev()
+            a_.record(stream)
+            pg.pg_attn_fwd(Lu, qu, ku, vu, w.softmax_scale, o=ou, lse=lu, stream=stream)
+            b_.record(stream)
+            ts.append((a_, b_))
+        torch.cuda.synchronize()
+        unpacked_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in ts]))
+        speedup = unpacked_ms / attn_avg
+        Lu.close()
+        del qu, ku, vu, ou, lu
+
+    traffic = load_traffic(w.name)
+    roof = {
+        "bound": "mfma",
+        "achieved": round(attn_tflops, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on a CPU sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, qkv, args.cpu_budget)
+
+    out = {
+        "metric": "packed shared-prefix attn fwd: useful TFLOP/s, % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "groups": w.num_groups,
+            "tokens": int(T),
+            "num_q_heads": int(Hq),
+            "num_kv_heads": int(Hkv),
+            "head_dim": int(d),
+            "useful_flop_per_step": useful_flop,
+            "useful_pairs": int(summ.useful_pairs),
+            "unpacked_pairs": int(summ.unpacked_pairs),
+            "work_items": int(summ.num_items),
+            "parallelism": "none (1 GPU)",
+            "input_sha256": {n: sha256(qkv[n])[:16] for n in ("q", "k", "v")},
+        },
+        "attn_only_tflops": round(attn_tflops, 2),
+        "pct_of_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "stage_ms": {
+            "layout_host": round(float(np.mean(layout_ms)), 4),
+            "position_ids": round(float(np.mean(pos_ms)), 4),
+            "rope": round(float(np.mean(rope_ms)), 4),
+            "attn_fwd": round(attn_avg, 4),
+        },
+        "rope_gbs": round(2 * T * (Hq + Hkv) * d * q.element_size() / (np.mean(rope_ms) * 1e-3) / 1e9, 1),
+        "unpacked_attn_ms": None if unpacked_ms is None else round(unpacked_ms, 4),
+        "speedup_vs_unpacked": None if speedup is None else round(speedup, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,218 @@
+/*
+ * pg.h -- C ABI of the packed shared-prefix attention library (libpg.so).
+ *
+ * The operation: a batch holds groups; each group is one prompt prefix stored
+ * once, followed by its response suffixes, all in one packed row of tokens
+ * ("Preference Packing: Efficient Preference Optimization for LLMs", core idea
+ * and technical framework). Prefix tokens attend causally within the prefix;
+ * a suffix token attends to the whole prefix and causally to its own suffix,
+ * never to a sibling suffix; position ids restart at the prefix length for
+ * every suffix (verl "prefix_grouper_utils.py" page, section 1 and the
+ * prefix-sharing diagram). Query blocks of all groups are scheduled as one
+ * launch over a work list balanced by masked-area FLOPs ("PackInfer", abstract).
+ *
+ * Conventions for every entry point:
+ *  - Packed token order: group 0 [prefix, suffix_1..suffix_n], group 1 [...],
+ *    no padding. T = sum of all prefix and suffix lengths.
+ *  - Device tensors are dense, row-major, caller-owned device pointers:
+ *      Q, Q_out, O : [T, Hq, d]    K, K_out, V : [T, Hkv, d]
+ *      lse         : [Hq, T] fp32  pos         : [T] int64
+ *    Q/K/V/O share one dtype (pg_dtype). Query head h reads KV head
+ *    h / (Hq / Hkv).
+ *  - Calls that take a stream enqueue work on it and return without waiting;
+ *    they never synchronise the device. Argument checks run before any launch.
+ *  - Errors come back as pg_status; no exception crosses the ABI. The text of
+ *    the last error of the calling thread is in pg_last_error().
+ *  - T = 0 (or zero groups) is legal: the compute calls return PG_OK and
+ *    launch nothing.
+ */
+#ifndef PG_H
+#define PG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pg_status {
+  PG_OK = 0,
+  PG_ERR_INVALID_ARG = -1, /* null pointer, negative length, bad head counts, overflow */
+  PG_ERR_UNSUPPORTED = -2, /* head_dim or dtype this build has no kernel for           */
+  PG_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed              */
+  PG_ERR_OOM = -4,         /* host or device allocation failed                         */
+  PG_ERR_STATE = -5        /* layout used on the device before pg_layout_upload        */
+} pg_status;
+
+typedef enum pg_dtype { PG_F32 = 0, PG_BF16 = 1 } pg_dtype;
+
+/* Opaque packed layout: offsets, per-token descriptors, the key spans and the
+ * FLOP-balanced work list. Immutable after it is built. */
+typedef struct pg_layout pg_layout;
+
+/* Summary of a built layout. */
+typedef struct pg_layout_summary {
+  int64_t total_tokens;    /* T                                                  */
+  int32_t num_groups;      /* G                                                  */
+  int32_t num_segments;    /* G + sum(suffix_counts): one prefix segment per group
+                              plus one per suffix, zero-length ones included     */
+  int32_t max_position;    /* largest position id (-1 when T = 0)                */
+  int32_t num_items;       /* work items of the attention launch                 */
+  int32_t num_spans;       /* key spans referenced by the work items             */
+  int32_t block_tokens;    /* query tokens per work item (at most)               */
+  int32_t heads_per_item;  /* query heads per work item                          */
+  int32_t device_ready;    /* 1 once the device copy exists                      */
+  int64_t useful_pairs;    /* allowed (query, key) pairs per query head; useful
+                              FLOP of the attention = 4 * d * Hq * useful_pairs  */
+  int64_t unpacked_pairs;  /* pairs of causal attention over every unpacked
+                              prefix+suffix sequence (the work packing avoids)   */
+  int64_t max_item_cost;   /* largest work item, in (query, key) pairs x heads   */
+} pg_layout_summary;
+
+/* One work item of the attention launch: query tokens [t0, t1) of one group,
+ * query heads [hq0, hq0 + heads_per_item), keys from spans
+ * [span0, span0 + nspan) of the span list. Items are stored in launch order. */
+typedef struct pg_work_item {
+  int32_t t0;
+  int32_t t1;
+  int32_t hq0;
+  int32_t pe;     /* end of the group's prefix (absolute token index)       */
+  int32_t span0;
+  int32_t nspan;
+  int64_t cost;   /* allowed (query, key) pairs of the item x its heads      */
+} pg_work_item;
+
+/* A contiguous key range [k0, k1) inside one segment of one group. */
+typedef struct pg_key_span {
+  int32_t k0;
+  int32_t k1;
+} pg_key_span;
+
+/*
+ * pg_build_layout_host -- build the packed layout on the host only.
+ *
+ * Follows the grouping of "Preference Packing" (technical framework: store each
+ * prompt once, then its responses) and the per-group prefix_len / suffix_lens
+ * of the layout object on the verl page (sections 1-2).
+ *
+ *  num_groups      G >= 0
+ *  prefix_lens     host int32 [G], each >= 0 (0: block-diagonal causal suffixes)
+ *  suffix_counts   host int32 [G], each >= 0 (0: the group is its prefix alone)
+ *  suffix_lens     host int32 [sum(suffix_counts)], each >= 0, group-major order;
+ *                  zero-length suffixes occupy no tokens
+ *  num_q_heads     Hq >= 1;  num_kv_heads Hkv >= 1 with Hq % Hkv == 0
+ *  head_dim        d in {64, 128}
+ *  rope_theta      > 0, base of the rotary frequencies used by pg_rope
+ *  out             receives the new layout (caller frees with pg_layout_destroy)
+ *
+ * T must not exceed 2^30. Arrays are copied; the caller keeps ownership.
+ * Returns PG_ERR_INVALID_ARG (bad argument), PG_ERR_UNSUPPORTED (head_dim),
+ * PG_ERR_OOM. *out is set to NULL on error.
+ */
+pg_status pg_build_layout_host(int32_t num_groups, const int32_t* prefix_lens,
+                               const int32_t* suffix_counts, const int32_t* suffix_lens,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               double rope_theta, pg_layout** out);
+
+/*
+ * pg_layout_upload -- copy the device part of a layout (per-token descriptors,
+ * work list, key spans, rotary frequencies) to the current HIP device, enqueued
+ * on `stream`. Allocates one device buffer owned by the layout. Calling it
+ * again is a no-op. PG_ERR_HIP / PG_ERR_OOM on failure.
+ */
+pg_status pg_layout_upload(pg_layout* layout, hipStream_t stream);
+
+/*
+ * pg_build_layout -- pg_build_layout_host followed by pg_layout_upload on
+ * `stream`: the layout builder of the packed path (group offsets, prefix and
+ * suffix spans, per-token descriptors and the work list of query blocks
+ * balanced by masked-area FLOPs, after the load-balanced execution groups of
+ * the "PackInfer" abstract).
+ */
+pg_status pg_build_layout(int32_t num_groups, const int32_t* prefix_lens,
+                          const int32_t* suffix_counts, const int32_t* suffix_lens,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          double rope_theta, hipStream_t stream, pg_layout** out);
+
+/* Fill *info. PG_ERR_INVALID_ARG on null. */
+pg_status pg_layout_info(const pg_layout* layout, pg_layout_summary* info);
+
+/* Host copies of the offsets: group_off [G+1] (first token of each group, then
+ * T) and seg_off [num_segments+1] (first token of each segment, then T).
+ * Either pointer may be NULL to skip it. */
+pg_status pg_layout_copy_offsets(const pg_layout* layout, int32_t* group_off, int32_t* seg_off);
+
+/* Host copies of the per-token descriptors, each [T] (any may be NULL):
+ * g0 = first token of the token's group, pe = end of that group's prefix,
+ * ss = first token of the token's own segment (g0 for prefix tokens). */
+pg_status pg_layout_copy_tokens(const pg_layout* layout, int32_t* g0, int32_t* pe, int32_t* ss);
+
+/* Host copies of the work list ([num_items], launch order) and of the key
+ * spans ([num_spans]); either may be NULL. */
+pg_status pg_layout_copy_work(const pg_layout* layout, pg_work_item* items, pg_key_span* spans);
+
+/* Free the layout and its device buffer. hipFree waits for the device, so
+ * no enqueued call that uses the layout is cut short. NULL is ignored. */
+void pg_layout_destroy(pg_layout* layout);
+
+/*
+ * pg_position_ids -- int64 position id of every packed token, on the device.
+ * verl page, section 1: a prefix token gets its index within the prefix; a
+ * suffix token gets prefix_len + its index within its own suffix, so every
+ * suffix restarts at prefix_len.
+ *  pos   device int64 [T], written completely.
+ * Needs an uploaded layout (PG_ERR_STATE otherwise).
+ */
+pg_status pg_position_ids(const pg_layout* layout, int64_t* pos, hipStream_t stream);
+
+/*
+ * pg_rope -- rotary embedding of Q and K at the given positions, one launch.
+ * The pages fix only the positions (verl page, section 1); the rotation is the
+ * rotate-half convention: for i < d/2, phi = pos * theta^(-2i/d) (computed in
+ * fp64), (x_i, x_{i+d/2}) -> (x_i cos phi - x_{i+d/2} sin phi,
+ *                             x_{i+d/2} cos phi + x_i sin phi),
+ * arithmetic in fp64, result rounded once to the tensor dtype (nearest-even).
+ * V is not touched.
+ *  pos           device int64 [T], any values >= 0 (normally pg_position_ids)
+ *  q_in, q_out   device [T, Hq, d];  k_in, k_out  device [T, Hkv, d]
+ *                q_out may equal q_in and k_out may equal k_in (in place);
+ *                other overlaps are not allowed.
+ *  dtype         PG_F32 or PG_BF16
+ */
+pg_status pg_rope(const pg_layout* layout, const int64_t* pos, const void* q_in,
+                  const void* k_in, void* q_out, void* k_out, pg_dtype dtype,
+                  hipStream_t stream);
+
+/*
+ * pg_attn_fwd -- packed shared-prefix causal attention, forward.
+ * For every token t and query head h: softmax over the allowed keys
+ * K(t) = { j : j in t's group, j <= t, and j is a prefix token or in t's own
+ * segment } of softmax_scale * <q[t,h], k[j,h/r]>, times v[j,h/r]; this equals
+ * causal attention over the unpacked sequence prefix || own suffix
+ * ("Preference Packing", core idea: prompt attention computed once and reused
+ * by every response; verl page, prefix-sharing diagram).
+ *  q, k, v   device inputs (layouts above), dtype `dtype`
+ *  o         device [T, Hq, d] output in `dtype`, written completely
+ *  lse       device fp32 [Hq, T]: ln(sum_j exp(softmax_scale * <q, k_j>)),
+ *            written completely; may be NULL to skip it
+ *  softmax_scale  finite, > 0
+ * bf16 runs on the MFMA kernel (d = 128) with fp32 accumulation; fp32 and
+ * bf16 with d = 64 run on a plain per-row kernel. Deterministic: every output
+ * element is written by exactly one thread, no atomics.
+ */
+pg_status pg_attn_fwd(const pg_layout* layout, const void* q, const void* k, const void* v,
+                      void* o, float* lse, pg_dtype dtype, float softmax_scale,
+                      hipStream_t stream);
+
+/* Static text for a status code. */
+const char* pg_status_string(pg_status status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* pg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PG_H */

@@ -1,0 +1,209 @@
+"""Thin Python binding of libpg.so: the same entry points as include/pg.h.
+
+Only argument marshalling happens here (shape/dtype checks, raw pointers,
+the current torch stream). Every step of the path runs in the library.
+torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import KeySpan, LayoutSummary, WorkItem, check, load
+
+
+def _i32(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+    if a.size and (a.min() < -(2**31) or a.max() >= 2**31):
+        raise ValueError("length does not fit int32")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def _ptr_i32(a: np.ndarray):
+    return a.ctypes.data_as(_lib.P_int32) if a.size else None
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class Layout:
+    """Owner of one pg_layout handle (freed on close / garbage collection)."""
+
+    def __init__(self, handle: int, heads: Tuple[int, int, int]):
+        self._h = ctypes.c_void_p(handle)
+        self.num_q_heads, self.num_kv_heads, self.head_dim = heads
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise ValueError("layout is closed")
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            load().pg_layout_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def summary(self) -> LayoutSummary:
+        s = LayoutSummary()
+        check(load().pg_layout_info(self.handle, ctypes.byref(s)), "pg_layout_info")
+        return s
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.summary().total_tokens)
+
+    def offsets(self) -> Tuple[np.ndarray, np.ndarray]:
+        s = self.summary()
+        g = np.zeros(s.num_groups + 1, dtype=np.int32)
+        seg = np.zeros(s.num_segments + 1, dtype=np.int32)
+        check(load().pg_layout_copy_offsets(self.handle, _ptr_i32(g), _ptr_i32(seg)),
+              "pg_layout_copy_offsets")
+        return g, seg
+
+    def tokens(self) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        T = self.total_tokens
+        g0, pe, ss = (np.zeros(T, dtype=np.int32) for _ in range(3))
+        check(load().pg_layout_copy_tokens(self.handle, _ptr_i32(g0), _ptr_i32(pe), _ptr_i32(ss)),
+              "pg_layout_copy_tokens")
+        return g0, pe, ss
+
+    def work(self) -> Tuple[np.ndarray, np.ndarray]:
+        """Work items (structured array, launch order) and key spans [n, 2]."""
+        s = self.summary()
+        items = (WorkItem * max(1, s.num_items))()
+        spans = (KeySpan * max(1, s.num_spans))()
+        check(load().pg_layout_copy_work(self.handle, items, spans), "pg_layout_copy_work")
+        it = np.frombuffer(items, dtype=np.dtype([("t0", "<i4"), ("t1", "<i4"), ("hq0", "<i4"),
+                                                  ("pe", "<i4"), ("span0", "<i4"),
+                                                  ("nspan", "<i4"), ("cost", "<i8")]))
+        sp = np.frombuffer(spans, dtype=np.int32).reshape(-1, 2)
+        return it[:s.num_items].copy(), sp[:s.num_spans].copy()
+
+
+def _layout_args(prefix_lens, suffix_counts, suffix_lens):
+    P, n, S = _i32(prefix_lens), _i32(suffix_counts), _i32(suffix_lens)
+    if P.shape != n.shape:
+        raise ValueError("prefix_lens and suffix_counts differ in length")
+    return P, n, S
+
+
+def pg_build_layout_host(prefix_lens: Sequence[int], suffix_counts: Sequence[int],
+                         suffix_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                         head_dim: int, rope_theta: float) -> Layout:
+    P, n, S = _layout_args(prefix_lens, suffix_counts, suffix_lens)
+    out = ctypes.c_void_p()
+    check(load().pg_build_layout_host(len(P), _ptr_i32(P), _ptr_i32(n), _ptr_i32(S),
+                                      num_q_heads, num_kv_heads, head_dim, float(rope_theta),
+                                      ctypes.byref(out)), "pg_build_layout_host")
+    return Layout(out.value, (num_q_heads, num_kv_heads, head_dim))
+
+
+def pg_layout_upload(layout: Layout, stream=None) -> None:
+    check(load().pg_layout_upload(layout.handle, _stream_handle(stream)), "pg_layout_upload")
+
+
+def pg_build_layout(prefix_lens: Sequence[int], suffix_counts: Sequence[int],
+                    suffix_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                    head_dim: int, rope_theta: float, stream=None) -> Layout:
+    P, n, S = _layout_args(prefix_lens, suffix_counts, suffix_lens)
+    out = ctypes.c_void_p()
+    check(load().pg_build_layout(len(P), _ptr_i32(P), _ptr_i32(n), _ptr_i32(S), num_q_heads,
+                                 num_kv_heads, head_dim, float(rope_theta),
+                                 _stream_handle(stream), ctypes.byref(out)), "pg_build_layout")
+    return Layout(out.value, (num_q_heads, num_kv_heads, head_dim))
+
+
+# ------------------------------------------------------------ device calls --
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _lib.PG_BF16
+    if t.dtype == torch.float32:
+        return _lib.PG_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_tensor(name, t, shape, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def pg_position_ids(layout: Layout, pos=None, stream=None):
+    """int64 [T] position ids on the current device."""
+    import torch
+    T = layout.total_tokens
+    if pos is None:
+        pos = torch.empty(T, dtype=torch.int64, device="cuda")
+    _check_tensor("pos", pos, (T,), torch.int64)
+    check(load().pg_position_ids(layout.handle, ctypes.c_void_p(pos.data_ptr()),
+                                 _stream_handle(stream)), "pg_position_ids")
+    return pos
+
+
+def pg_rope(layout: Layout, pos, q, k, q_out=None, k_out=None, stream=None):
+    """RoPE of q [T, Hq, d] and k [T, Hkv, d] at `pos`; out-of-place unless
+    q_out is q / k_out is k."""
+    import torch
+    T, Hq, Hkv, d = layout.total_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    _check_tensor("pos", pos, (T,), torch.int64)
+    _check_tensor("q", q, (T, Hq, d))
+    _check_tensor("k", k, (T, Hkv, d), q.dtype)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    _check_tensor("q_out", q_out, (T, Hq, d), q.dtype)
+    _check_tensor("k_out", k_out, (T, Hkv, d), q.dtype)
+    check(load().pg_rope(layout.handle, ctypes.c_void_p(pos.data_ptr()),
+                         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                         ctypes.c_void_p(q_out.data_ptr()), ctypes.c_void_p(k_out.data_ptr()),
+                         _dtype_code(q), _stream_handle(stream)), "pg_rope")
+    return q_out, k_out
+
+
+def pg_attn_fwd(layout: Layout, q, k, v, softmax_scale: float, o=None, lse=None,
+                want_lse: bool = True, stream=None):
+    """Packed attention forward. Returns (o [T, Hq, d], lse fp32 [Hq, T] or None)."""
+    import torch
+    T, Hq, Hkv, d = layout.total_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    _check_tensor("q", q, (T, Hq, d))
+    _check_tensor("k", k, (T, Hkv, d), q.dtype)
+    _check_tensor("v", v, (T, Hkv, d), q.dtype)
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, (T, Hq, d), q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_tensor("lse", lse, (Hq, T), torch.float32)
+    check(load().pg_attn_fwd(layout.handle, ctypes.c_void_p(q.data_ptr()),
+                             ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                             ctypes.c_void_p(o.data_ptr()),
+                             ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                             _dtype_code(q), float(softmax_scale), _stream_handle(stream)),
+          "pg_attn_fwd")
+    return o, lse

@@ -1,0 +1,247 @@
+// C ABI of libpg.so: argument checks, error text, the layout's device copy,
+// and dispatch to the HIP launchers. Exceptions never cross this boundary.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "pg_internal.h"
+
+namespace {
+thread_local std::string g_last_error;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+pg_status hip_fail(hipError_t e, const char* what) {
+  return pg_fail(PG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Device-side checks shared by the compute entry points.
+pg_status check_device_layout(const pg_layout* L) {
+  if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
+  if (!L->dev_buf && L->T > 0)
+    return pg_fail(PG_ERR_STATE, "layout has no device copy (call pg_layout_upload)");
+  if (L->T > 0) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != L->device)
+      return pg_fail(PG_ERR_STATE, "layout lives on device %d, current device is %d", L->device, dev);
+  }
+  return PG_OK;
+}
+}  // namespace
+
+pg_status pg_fail(pg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  try {
+    g_last_error = buf;
+  } catch (...) {
+  }
+  return s;
+}
+
+void pg_clear_error() { g_last_error.clear(); }
+
+extern "C" {
+
+const char* pg_status_string(pg_status s) {
+  switch (s) {
+    case PG_OK: return "ok";
+    case PG_ERR_INVALID_ARG: return "invalid argument";
+    case PG_ERR_UNSUPPORTED: return "unsupported";
+    case PG_ERR_HIP: return "HIP error";
+    case PG_ERR_OOM: return "out of memory";
+    case PG_ERR_STATE: return "bad state";
+  }
+  return "unknown status";
+}
+
+const char* pg_last_error(void) { return g_last_error.c_str(); }
+
+pg_status pg_build_layout_host(int32_t num_groups, const int32_t* prefix_lens,
+                               const int32_t* suffix_counts, const int32_t* suffix_lens,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               double rope_theta, pg_layout** out) {
+  if (!out) return pg_fail(PG_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  pg_clear_error();
+  pg_layout* L = new (std::nothrow) pg_layout();
+  if (!L) return pg_fail(PG_ERR_OOM, "host allocation failed");
+  pg_status s = pg_layout_build_host(*L, num_groups, prefix_lens, suffix_counts, suffix_lens,
+                                     num_q_heads, num_kv_heads, head_dim, rope_theta);
+  if (s != PG_OK) {
+    delete L;
+    return s;
+  }
+  *out = L;
+  return PG_OK;
+}
+
+pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
+  if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
+  if (L->dev_buf || L->T == 0) {
+    if (L->T == 0 && L->device < 0) {
+      hipError_t e = hipGetDevice(&L->device);
+      if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    }
+    return PG_OK;
+  }
+  const size_t A = 256;
+  const size_t T = size_t(L->T);
+  const size_t off_g0 = 0;
+  const size_t off_pe = align_up(off_g0 + 4 * T, A);
+  const size_t off_ss = align_up(off_pe + 4 * T, A);
+  const size_t off_it = align_up(off_ss + 4 * T, A);
+  const size_t off_sp = align_up(off_it + sizeof(pg_work_item) * L->items.size(), A);
+  const size_t off_fr = align_up(off_sp + sizeof(pg_key_span) * L->spans.size(), A);
+  const size_t bytes = align_up(off_fr + sizeof(double) * L->inv_freq.size(), A);
+  try {
+    L->staging.assign(bytes, 0);
+  } catch (const std::bad_alloc&) {
+    return pg_fail(PG_ERR_OOM, "host staging allocation failed");
+  }
+  unsigned char* h = L->staging.data();
+  std::memcpy(h + off_g0, L->tok_g0.data(), 4 * T);
+  std::memcpy(h + off_pe, L->tok_pe.data(), 4 * T);
+  std::memcpy(h + off_ss, L->tok_ss.data(), 4 * T);
+  if (!L->items.empty())
+    std::memcpy(h + off_it, L->items.data(), sizeof(pg_work_item) * L->items.size());
+  if (!L->spans.empty())
+    std::memcpy(h + off_sp, L->spans.data(), sizeof(pg_key_span) * L->spans.size());
+  std::memcpy(h + off_fr, L->inv_freq.data(), sizeof(double) * L->inv_freq.size());
+
+  hipError_t e = hipGetDevice(&L->device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* d = nullptr;
+  e = hipMalloc(&d, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? pg_fail(PG_ERR_OOM, "hipMalloc(%zu) failed", bytes)
+                                    : hip_fail(e, "hipMalloc");
+  }
+  e = hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    return hip_fail(e, "hipMemcpyAsync");
+  }
+  unsigned char* b = static_cast<unsigned char*>(d);
+  L->dev_buf = d;
+  L->d_g0 = reinterpret_cast<const int32_t*>(b + off_g0);
+  L->d_pe = reinterpret_cast<const int32_t*>(b + off_pe);
+  L->d_ss = reinterpret_cast<const int32_t*>(b + off_ss);
+  L->d_items = reinterpret_cast<const pg_work_item*>(b + off_it);
+  L->d_spans = reinterpret_cast<const pg_key_span*>(b + off_sp);
+  L->d_inv_freq = reinterpret_cast<const double*>(b + off_fr);
+  return PG_OK;
+}
+
+pg_status pg_build_layout(int32_t num_groups, const int32_t* prefix_lens,
+                          const int32_t* suffix_counts, const int32_t* suffix_lens,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          double rope_theta, hipStream_t stream, pg_layout** out) {
+  pg_status s = pg_build_layout_host(num_groups, prefix_lens, suffix_counts, suffix_lens,
+                                     num_q_heads, num_kv_heads, head_dim, rope_theta, out);
+  if (s != PG_OK) return s;
+  s = pg_layout_upload(*out, stream);
+  if (s != PG_OK) {
+    pg_layout_destroy(*out);
+    *out = nullptr;
+  }
+  return s;
+}
+
+pg_status pg_layout_info(const pg_layout* L, pg_layout_summary* info) {
+  if (!L || !info) return pg_fail(PG_ERR_INVALID_ARG, "NULL argument");
+  info->total_tokens = L->T;
+  info->num_groups = L->G;
+  info->num_segments = L->num_segments;
+  info->max_position = L->max_position;
+  info->num_items = int32_t(L->items.size());
+  info->num_spans = int32_t(L->spans.size());
+  info->block_tokens = L->block_tokens;
+  info->heads_per_item = L->heads_per_item;
+  info->device_ready = (L->dev_buf != nullptr || (L->T == 0 && L->device >= 0)) ? 1 : 0;
+  info->useful_pairs = L->useful_pairs;
+  info->unpacked_pairs = L->unpacked_pairs;
+  info->max_item_cost = L->max_item_cost;
+  return PG_OK;
+}
+
+pg_status pg_layout_copy_offsets(const pg_layout* L, int32_t* group_off, int32_t* seg_off) {
+  if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
+  if (group_off) std::memcpy(group_off, L->group_off.data(), 4 * L->group_off.size());
+  if (seg_off) std::memcpy(seg_off, L->seg_off.data(), 4 * L->seg_off.size());
+  return PG_OK;
+}
+
+pg_status pg_layout_copy_tokens(const pg_layout* L, int32_t* g0, int32_t* pe, int32_t* ss) {
+  if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
+  const size_t n = 4 * size_t(L->T);
+  if (g0 && n) std::memcpy(g0, L->tok_g0.data(), n);
+  if (pe && n) std::memcpy(pe, L->tok_pe.data(), n);
+  if (ss && n) std::memcpy(ss, L->tok_ss.data(), n);
+  return PG_OK;
+}
+
+pg_status pg_layout_copy_work(const pg_layout* L, pg_work_item* items, pg_key_span* spans) {
+  if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
+  if (items && !L->items.empty())
+    std::memcpy(items, L->items.data(), sizeof(pg_work_item) * L->items.size());
+  if (spans && !L->spans.empty())
+    std::memcpy(spans, L->spans.data(), sizeof(pg_key_span) * L->spans.size());
+  return PG_OK;
+}
+
+void pg_layout_destroy(pg_layout* L) {
+  if (!L) return;
+  if (L->dev_buf) (void)hipFree(L->dev_buf);
+  delete L;
+}
+
+pg_status pg_position_ids(const pg_layout* L, int64_t* pos, hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (L->T == 0) return PG_OK;
+  if (!pos) return pg_fail(PG_ERR_INVALID_ARG, "pos is NULL");
+  hipError_t e = pg_launch_positions(*L, pos, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "position-id kernel launch");
+}
+
+pg_status pg_rope(const pg_layout* L, const int64_t* pos, const void* q_in, const void* k_in,
+                  void* q_out, void* k_out, pg_dtype dtype, hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (dtype != PG_F32 && dtype != PG_BF16)
+    return pg_fail(PG_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (L->T == 0) return PG_OK;
+  if (!pos || !q_in || !k_in || !q_out || !k_out)
+    return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e = pg_launch_rope(*L, pos, q_in, k_in, q_out, k_out, dtype, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "rope kernel launch");
+}
+
+pg_status pg_attn_fwd(const pg_layout* L, const void* q, const void* k, const void* v, void* o,
+                      float* lse, pg_dtype dtype, float softmax_scale, hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (dtype != PG_F32 && dtype != PG_BF16)
+    return pg_fail(PG_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return pg_fail(PG_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (L->T == 0) return PG_OK;
+  if (!q || !k || !v || !o) return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e;
+  if (dtype == PG_BF16 && L->d == 128)
+    e = pg_launch_attn_mfma(*L, q, k, v, o, lse, softmax_scale, stream);
+  else
+    e = pg_launch_attn_rowwise(*L, q, k, v, o, lse, dtype, softmax_scale, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "attention kernel launch");
+}
+
+}  // extern "C"

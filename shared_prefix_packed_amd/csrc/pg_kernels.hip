@@ -1,0 +1,254 @@
+// Position ids, rotary embedding and the plain per-row attention kernel.
+//
+// Position ids follow the verl prefix_grouper_utils.py page (section 1,
+// building position ids): prefix tokens count from 0, every suffix restarts at
+// the prefix length. RoPE is applied at those positions (the pages never define
+// RoPE; rotate-half convention). The per-row attention kernel evaluates the
+// packed key set of every token directly (fp32, and bf16 with d = 64).
+#include <hip/hip_runtime.h>
+
+#include "pg_internal.h"
+
+namespace {
+
+// ------------------------------------------------------------- positions --
+// One thread per token: pos = t - g0 in the prefix, P + (t - ss) in a suffix.
+__global__ __launch_bounds__(256) void positions_kernel(const int32_t* __restrict__ g0,
+                                                        const int32_t* __restrict__ pe,
+                                                        const int32_t* __restrict__ ss,
+                                                        int64_t* __restrict__ pos, int32_t T) {
+  const int32_t t = int32_t(blockIdx.x) * 256 + int32_t(threadIdx.x);
+  if (t >= T) return;
+  const int32_t a = g0[t], p = pe[t];
+  pos[t] = t < p ? int64_t(t - a) : int64_t(p - a) + int64_t(t - ss[t]);
+}
+
+// ------------------------------------------------------------------ RoPE --
+// A workgroup handles ROPE_TOK tokens. First every (token, i) angle's cos/sin
+// is taken in fp64 and parked in LDS; then each thread rotates chunks of 8
+// pairs (x_i.., x_{i+d/2}..) of one head with 16-byte loads for bf16. The
+// rotation runs in fp64 and is rounded once to the storage dtype: in fp32,
+// x cos - y sin loses to cancellation near zero more than a bf16 ulp there.
+constexpr int ROPE_TOK = 4;
+
+// fp64 -> bf16 bits, nearest-even, in one rounding (no detour through fp32).
+__device__ inline uint32_t f64_to_bf16_bits(double x) {
+  const uint64_t u = uint64_t(__double_as_longlong(x));
+  const uint64_t mag = u & 0x7fffffffffffffffull;
+  const uint32_t sign = uint32_t(u >> 48) & 0x8000u;
+  if (mag < 0x3810000000000000ull) {   // |x| < 2^-126: below bf16 normals
+    const uint32_t f = __float_as_uint(float(x));   // tiny values go through fp32
+    return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16;
+  }
+  // keep 7 mantissa bits: round at bit 45 of the fp64 pattern, ties to even
+  const uint64_t r = (mag + ((uint64_t(1) << 44) - 1) + ((mag >> 45) & 1)) >> 45;   // exp11|mant7
+  const uint32_t e = uint32_t(r >> 7);                                                // fp64 exponent
+  if (e >= 1023 + 128) return sign | 0x7f80u;                                         // overflow: inf
+  return sign | ((e - 1023 + 127) << 7) | uint32_t(r & 0x7f);
+}
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<uint16_t> {   // 8 bf16 as raw bits
+  uint4 v;
+  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ void store(uint16_t* p) const { *reinterpret_cast<uint4*>(p) = v; }
+  __device__ double get(int e) const {
+    const uint32_t w = (&v.x)[e >> 1];
+    return double(__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)));
+  }
+  __device__ void set2(int m, double a, double b) {
+    (&v.x)[m] = f64_to_bf16_bits(a) | (f64_to_bf16_bits(b) << 16);
+  }
+};
+template <>
+struct Vec8<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ void store(float* p) const {
+    *reinterpret_cast<float4*>(p) = a;
+    *reinterpret_cast<float4*>(p + 4) = b;
+  }
+  __device__ double get(int e) const { return double(e < 4 ? (&a.x)[e] : (&b.x)[e - 4]); }
+  __device__ void set2(int m, double x, double y) {
+    float* f = m < 2 ? &a.x : &b.x;
+    f[(2 * m) & 3] = float(x);
+    f[(2 * m + 1) & 3] = float(y);
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_kernel(const int64_t* __restrict__ pos,
+                                                   const double* __restrict__ inv_freq,
+                                                   const T* q_in, const T* k_in, T* q_out,
+                                                   T* k_out, int32_t Ttok, int32_t Hq,
+                                                   int32_t Hkv) {
+  constexpr int HALF = D / 2;
+  constexpr int NCH = HALF / 8;
+  __shared__ double cs[ROPE_TOK][HALF];
+  __shared__ double sn[ROPE_TOK][HALF];
+  const int64_t tbase = int64_t(blockIdx.x) * ROPE_TOK;
+  for (int e = threadIdx.x; e < ROPE_TOK * HALF; e += 256) {
+    const int tt = e / HALF, i = e % HALF;
+    const int64_t t = tbase + tt;
+    double s = 0.0, c = 1.0;
+    if (t < Ttok) sincos(double(pos[t]) * inv_freq[i], &s, &c);
+    cs[tt][i] = c;
+    sn[tt][i] = s;
+  }
+  __syncthreads();
+  const int heads = Hq + Hkv;
+  const int tasks = ROPE_TOK * heads * NCH;
+  for (int task = threadIdx.x; task < tasks; task += 256) {
+    const int tt = task / (heads * NCH);
+    const int rem = task - tt * heads * NCH;
+    const int hh = rem / NCH;
+    const int ch = rem - hh * NCH;
+    const int64_t t = tbase + tt;
+    if (t >= Ttok) continue;
+    const T* src;
+    T* dst;
+    if (hh < Hq) {
+      src = q_in + (t * Hq + hh) * D;
+      dst = q_out + (t * Hq + hh) * D;
+    } else {
+      src = k_in + (t * Hkv + (hh - Hq)) * D;
+      dst = k_out + (t * Hkv + (hh - Hq)) * D;
+    }
+    Vec8<T> lo, hi, ylo, yhi;
+    lo.load(src + ch * 8);
+    hi.load(src + HALF + ch * 8);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      double rl[2], rh[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int e = 2 * m + e2;
+        const double c = cs[tt][ch * 8 + e], s = sn[tt][ch * 8 + e];
+        const double xl = lo.get(e), xh = hi.get(e);
+        rl[e2] = xl * c - xh * s;
+        rh[e2] = xh * c + xl * s;
+      }
+      ylo.set2(m, rl[0], rl[1]);
+      yhi.set2(m, rh[0], rh[1]);
+    }
+    ylo.store(dst + ch * 8);
+    yhi.store(dst + HALF + ch * 8);
+  }
+}
+
+// ------------------------------------------------------ per-row attention --
+// One wave per (token, query head). Lanes split the head dimension; the wave
+// walks the token's key set K(t) = [g0, pe) u [ss, t] (prefix tokens: [g0, t])
+// with an online softmax in base 2. Reference-grade speed, used for fp32 and
+// for bf16 with d = 64.
+template <typename T>
+__device__ inline float to_f(T x);
+template <>
+__device__ inline float to_f<float>(float x) { return x; }
+template <>
+__device__ inline float to_f<uint16_t>(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+template <typename T>
+__device__ inline T from_f(float x);
+template <>
+__device__ inline float from_f<float>(float x) { return x; }
+template <>
+__device__ inline uint16_t from_f<uint16_t>(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_rowwise_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
+    float* __restrict__ lse, const int32_t* __restrict__ g0a, const int32_t* __restrict__ pea,
+    const int32_t* __restrict__ ssa, int32_t Ttok, int32_t Hq, int32_t Hkv, float c_log2) {
+  constexpr int E = D / 64;
+  const int64_t idx = blockIdx.x;
+  const int32_t t = int32_t(idx / Hq);
+  const int32_t h = int32_t(idx % Hq);
+  const int32_t hk = h / (Hq / Hkv);
+  const int lane = threadIdx.x;
+  float qv[E], acc[E];
+  const T* qr = q + (int64_t(t) * Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qv[e] = to_f<T>(qr[lane * E + e]);
+    acc[e] = 0.f;
+  }
+  const int32_t g0 = g0a[t], pe = pea[t], ss = ssa[t];
+  float m = -1.0e30f, l = 0.f;
+  for (int32_t j = g0; j <= t; ++j) {
+    if (j >= pe && j < ss) j = ss;   // skip sibling suffixes (ss <= t always)
+    const T* kr = k + (int64_t(j) * Hkv + hk) * D;
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) part += qv[e] * to_f<T>(kr[lane * E + e]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    const float s = part * c_log2;
+    const float mn = fmaxf(m, s);
+    const float alpha = exp2f(m - mn);
+    const float p = exp2f(s - mn);
+    l = l * alpha + p;
+    const T* vr = v + (int64_t(j) * Hkv + hk) * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = acc[e] * alpha + p * to_f<T>(vr[lane * E + e]);
+    m = mn;
+  }
+  const float inv = 1.f / l;
+  T* orow = o + (int64_t(t) * Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) orow[lane * E + e] = from_f<T>(acc[e] * inv);
+  if (lse && lane == 0) lse[int64_t(h) * Ttok + t] = (m + log2f(l)) * 0.69314718055994530942f;
+}
+
+}  // namespace
+
+hipError_t pg_launch_positions(const pg_layout& L, int64_t* pos, hipStream_t stream) {
+  const int32_t T = int32_t(L.T);
+  positions_kernel<<<dim3((T + 255) / 256), dim3(256), 0, stream>>>(L.d_g0, L.d_pe, L.d_ss, pos, T);
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_rope(const pg_layout& L, const int64_t* pos, const void* q_in,
+                          const void* k_in, void* q_out, void* k_out, pg_dtype dtype,
+                          hipStream_t stream) {
+  const int32_t T = int32_t(L.T);
+  const dim3 grid((T + ROPE_TOK - 1) / ROPE_TOK), block(256);
+#define PG_ROPE(TY, DD)                                                                       \
+  rope_kernel<TY, DD><<<grid, block, 0, stream>>>(                                            \
+      pos, L.d_inv_freq, static_cast<const TY*>(q_in), static_cast<const TY*>(k_in),          \
+      static_cast<TY*>(q_out), static_cast<TY*>(k_out), T, L.Hq, L.Hkv)
+  if (dtype == PG_BF16) {
+    if (L.d == 128) PG_ROPE(uint16_t, 128); else PG_ROPE(uint16_t, 64);
+  } else {
+    if (L.d == 128) PG_ROPE(float, 128); else PG_ROPE(float, 64);
+  }
+#undef PG_ROPE
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_attn_rowwise(const pg_layout& L, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, pg_dtype dtype,
+                                  float softmax_scale, hipStream_t stream) {
+  const int64_t blocks = L.T * L.Hq;
+  if (blocks > int64_t(0x7fffffff)) return hipErrorInvalidConfiguration;
+  const float c = softmax_scale * 1.44269504088896340736f;
+  const int32_t T = int32_t(L.T);
+#define PG_ROW(TY, DD)                                                                        \
+  attn_rowwise_kernel<TY, DD><<<dim3(uint32_t(blocks)), dim3(64), 0, stream>>>(             \
+      static_cast<const TY*>(q), static_cast<const TY*>(k), static_cast<const TY*>(v),        \
+      static_cast<TY*>(o), lse, L.d_g0, L.d_pe, L.d_ss, T, L.Hq, L.Hkv, c)
+  if (dtype == PG_BF16) {
+    if (L.d == 128) PG_ROW(uint16_t, 128); else PG_ROW(uint16_t, 64);
+  } else {
+    if (L.d == 128) PG_ROW(float, 128); else PG_ROW(float, 64);
+  }
+#undef PG_ROW
+  return hipGetLastError();
+}

@@ -1,0 +1,201 @@
+// Host layout builder: offsets, per-token descriptors, key spans and the
+// FLOP-balanced work list of the attention launch.
+//
+// Layout: "Preference Packing" (technical framework) stores each prompt once,
+// followed by its responses; the verl prefix_grouper_utils.py page describes
+// the grouped batch by per-group prefix_len and suffix_lens (sections 1-2).
+// Work list: query blocks of all groups go into one launch, ordered so the
+// hardware dispatcher balances them ("PackInfer", abstract: batched requests
+// organised into load-balanced execution groups, one unified kernel launch,
+// thread-block execution balanced, shared-prefix requests co-located).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+
+#include "pg_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 30;   // keeps every int32 key index + tile size in range
+
+int gcd_int(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Allowed keys of one query token: the group prefix up to the token for
+// prefix tokens; the whole prefix plus its own segment up to itself for
+// suffix tokens.
+inline int64_t keys_of(int32_t t, int32_t g0, int32_t pe, int32_t ss) {
+  if (t < pe) return int64_t(t - g0 + 1);
+  return int64_t(pe - g0) + int64_t(t - ss + 1);
+}
+
+}  // namespace
+
+pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* prefix_lens,
+                               const int32_t* suffix_counts, const int32_t* suffix_lens,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               double rope_theta) {
+  // ---------------------------------------------------------- validation --
+  if (num_groups < 0) return pg_fail(PG_ERR_INVALID_ARG, "num_groups %d < 0", num_groups);
+  if (num_groups > 0 && (!prefix_lens || !suffix_counts))
+    return pg_fail(PG_ERR_INVALID_ARG, "prefix_lens / suffix_counts is NULL");
+  if (num_q_heads < 1 || num_kv_heads < 1)
+    return pg_fail(PG_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", num_q_heads,
+                   num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return pg_fail(PG_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", num_q_heads,
+                   num_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return pg_fail(PG_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return pg_fail(PG_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+
+  int64_t nsuf = 0, total = 0;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    if (prefix_lens[g] < 0) return pg_fail(PG_ERR_INVALID_ARG, "prefix_lens[%d] < 0", g);
+    if (suffix_counts[g] < 0) return pg_fail(PG_ERR_INVALID_ARG, "suffix_counts[%d] < 0", g);
+    nsuf += suffix_counts[g];
+    total += prefix_lens[g];
+    if (nsuf > kMaxTokens || total > kMaxTokens)
+      return pg_fail(PG_ERR_INVALID_ARG, "layout too large");
+  }
+  if (nsuf > 0 && !suffix_lens) return pg_fail(PG_ERR_INVALID_ARG, "suffix_lens is NULL");
+  for (int64_t i = 0; i < nsuf; ++i) {
+    if (suffix_lens[i] < 0) return pg_fail(PG_ERR_INVALID_ARG, "suffix_lens[%lld] < 0", (long long)i);
+    total += suffix_lens[i];
+    if (total > kMaxTokens)
+      return pg_fail(PG_ERR_INVALID_ARG, "total tokens exceed 2^30");
+  }
+
+  try {
+    L.G = num_groups;
+    L.Hq = num_q_heads;
+    L.Hkv = num_kv_heads;
+    L.d = head_dim;
+    L.T = total;
+    L.rope_theta = rope_theta;
+    L.prefix_lens.assign(prefix_lens, prefix_lens + num_groups);
+    L.suffix_counts.assign(suffix_counts, suffix_counts + num_groups);
+    L.suffix_lens.assign(suffix_lens, suffix_lens + nsuf);
+    L.num_segments = int32_t(num_groups + nsuf);
+
+    // ------------------------------------------------ offsets + tokens ----
+    L.group_off.assign(size_t(num_groups) + 1, 0);
+    L.seg_off.clear();
+    L.seg_off.reserve(size_t(L.num_segments) + 1);
+    L.tok_g0.resize(size_t(total));
+    L.tok_pe.resize(size_t(total));
+    L.tok_ss.resize(size_t(total));
+    L.max_position = -1;
+    L.useful_pairs = 0;
+    L.unpacked_pairs = 0;
+    int32_t cur = 0;
+    int64_t k = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const int32_t g0 = cur, P = prefix_lens[g], pe = g0 + P;
+      L.group_off[g] = g0;
+      L.seg_off.push_back(g0);
+      for (int32_t t = g0; t < pe; ++t) {
+        L.tok_g0[t] = g0;
+        L.tok_pe[t] = pe;
+        L.tok_ss[t] = g0;
+      }
+      if (P > 0) L.max_position = std::max(L.max_position, P - 1);
+      const int64_t Pl = P;
+      L.useful_pairs += Pl * (Pl + 1) / 2;
+      cur = pe;
+      if (suffix_counts[g] == 0) L.unpacked_pairs += Pl * (Pl + 1) / 2;
+      for (int32_t j = 0; j < suffix_counts[g]; ++j, ++k) {
+        const int32_t S = suffix_lens[k];
+        L.seg_off.push_back(cur);
+        for (int32_t t = cur; t < cur + S; ++t) {
+          L.tok_g0[t] = g0;
+          L.tok_pe[t] = pe;
+          L.tok_ss[t] = cur;
+        }
+        if (S > 0) L.max_position = std::max(L.max_position, P + S - 1);
+        const int64_t Sl = S;
+        L.useful_pairs += Sl * Pl + Sl * (Sl + 1) / 2;
+        L.unpacked_pairs += (Pl + Sl) * (Pl + Sl + 1) / 2;
+        cur += S;
+      }
+    }
+    L.group_off[num_groups] = cur;
+    L.seg_off.push_back(cur);
+
+    // ------------------------------------------------ rotary frequencies --
+    L.inv_freq.resize(size_t(head_dim / 2));
+    for (int i = 0; i < head_dim / 2; ++i)
+      L.inv_freq[i] = std::pow(rope_theta, -2.0 * double(i) / double(head_dim));
+
+    // --------------------------------------------------------- work list --
+    // One item = query tokens [t0, t1) of one group x `hpw` query heads of one
+    // KV head. hpw = gcd(r, 4) heads share each LDS K/V tile (GQA reuse); the
+    // four waves of an item cover hpw heads x (4 / hpw) blocks of 32 tokens.
+    const int r = num_q_heads / num_kv_heads;
+    const int hpw = gcd_int(r, PG_ITEM_WAVES);
+    const int BT = PG_WAVE_QUERIES * PG_ITEM_WAVES / hpw;
+    L.heads_per_item = hpw;
+    L.block_tokens = BT;
+    L.items.clear();
+    L.spans.clear();
+    L.max_item_cost = 0;
+    k = 0;
+    int32_t seg = 0;   // index of the group's prefix segment in seg_off
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const int32_t g0 = L.group_off[g], g1 = L.group_off[g + 1];
+      const int32_t pe = g0 + prefix_lens[g];
+      const int32_t nseg = suffix_counts[g];
+      int32_t first_suffix = 0;   // first suffix segment that may still overlap a block
+      for (int32_t t0 = g0; t0 < g1; t0 += BT) {
+        const int32_t t1 = std::min<int32_t>(t0 + BT, g1);
+        const int32_t span0 = int32_t(L.spans.size());
+        if (pe > g0) L.spans.push_back({g0, std::min(pe, t1)});
+        while (first_suffix < nseg && L.seg_off[seg + 2 + first_suffix] <= t0) ++first_suffix;
+        for (int32_t j = first_suffix; j < nseg; ++j) {
+          const int32_t a = L.seg_off[seg + 1 + j], b = L.seg_off[seg + 2 + j];
+          if (a >= t1) break;
+          if (b > a && b > t0) L.spans.push_back({a, std::min(b, t1)});
+        }
+        const int32_t nspan = int32_t(L.spans.size()) - span0;
+        int64_t pairs = 0;
+        for (int32_t t = t0; t < t1; ++t) pairs += keys_of(t, L.tok_g0[t], L.tok_pe[t], L.tok_ss[t]);
+        for (int32_t hk = 0; hk < num_kv_heads; ++hk) {
+          for (int32_t sub = 0; sub < r / hpw; ++sub) {
+            pg_work_item it;
+            it.t0 = t0;
+            it.t1 = t1;
+            it.hq0 = hk * r + sub * hpw;
+            it.pe = pe;
+            it.span0 = span0;
+            it.nspan = nspan;
+            it.cost = pairs * hpw;
+            L.max_item_cost = std::max(L.max_item_cost, it.cost);
+            L.items.push_back(it);
+          }
+        }
+      }
+      seg += 1 + nseg;
+      k += nseg;
+    }
+    // Longest-processing-time order: the dispatcher hands the next item to
+    // the first free slot, so cost-descending order is greedy LPT. Ties keep
+    // a fixed (t0, hq0) order so the list is deterministic.
+    std::stable_sort(L.items.begin(), L.items.end(),
+                     [](const pg_work_item& a, const pg_work_item& b) {
+                       if (a.cost != b.cost) return a.cost > b.cost;
+                       if (a.t0 != b.t0) return a.t0 < b.t0;
+                       return a.hq0 < b.hq0;
+                     });
+  } catch (const std::bad_alloc&) {
+    return pg_fail(PG_ERR_OOM, "host allocation failed");
+  }
+  return PG_OK;
+}

@@ -1,0 +1,345 @@
+"""GPU parity of libpg.so against the fp64 oracle.
+
+Tolerances (stated for this path): position ids and layout bit-exact; RoPE
+within 1 ulp of the storage dtype (bf16: count of 1-ulp differences reported
+and bounded; fp32: 1e-6 abs); attention output O max-abs error <= 2e-2 and
+lse error <= 1e-3, for fp32 and bf16.
+
+Small workloads are checked element by element against the full oracle; the
+full-size workloads on sampled (token, head) rows that the oracle computes one
+at a time by the definition (plus every group's first and last token and
+tile-boundary tokens), in the same launch configuration the benchmark times.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import shared_prefix_packed_amd as pg
+from oracle import pg_oracle as O
+from workloads import bf16_bits_to_f32, draw_qkv, make_custom, make_workload
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(w, a):
+    if w.dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def to_host_f32(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(t.view(torch.int16).numpy().view(np.uint16))
+    return t.numpy().astype(np.float32)
+
+
+def host_vals(w, a):
+    return bf16_bits_to_f32(a) if w.dtype == "bf16" else a
+
+
+def layout_of(w):
+    return pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
+                              w.num_kv_heads, w.head_dim, w.rope_theta)
+
+
+def oracle_layout(w):
+    return O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+
+
+_cache = {}
+
+
+def workload_inputs(i):
+    if i not in _cache:
+        w = make_workload(i)
+        _cache.clear()
+        _cache[i] = (w, draw_qkv(w))
+    return _cache[i]
+
+
+def sample_rows(lay, T, Hq, n, seed):
+    """Random (token, head) pairs plus structural edge tokens."""
+    r = np.random.default_rng(seed)
+    toks = list(r.integers(0, T, size=n))
+    for a in lay["seg_off"]:
+        for t in (a - 1, a, a + 1, a + 31, a + 32, a + 63, a + 64):
+            if 0 <= t < T:
+                toks.append(int(t))
+    toks = sorted(set(int(t) for t in toks))
+    heads = list(r.integers(0, Hq, size=len(toks)))
+    # always include first and last head somewhere
+    if toks:
+        heads[0] = 0
+        heads[-1] = Hq - 1
+    return toks, heads
+
+
+def check_attn(w, o_gpu, lse_gpu, q, k, v, lay, full):
+    """Compare GPU (o, lse) with the oracle on all rows (full) or a sample."""
+    Hq = w.num_q_heads
+    o_g = to_host_f32(o_gpu)
+    l_g = lse_gpu.detach().cpu().numpy()
+    if full:
+        o_ref, l_ref = O.attention(q, k, v, lay, w.softmax_scale, Hq, w.num_kv_heads)
+        eo = np.abs(o_g.astype(np.float64) - o_ref).max()
+        el = np.abs(l_g.astype(np.float64) - l_ref).max()
+    else:
+        toks, heads = sample_rows(lay, w.total_tokens, Hq, 300, 17 + max(w.index, 0))
+        o_ref, l_ref = O.attention_rows(q, k, v, lay, w.softmax_scale, Hq, w.num_kv_heads,
+                                        toks, heads)
+        eo = np.abs(o_g[toks, heads].astype(np.float64) - o_ref).max()
+        el = np.abs(l_g[heads, toks].astype(np.float64) - l_ref).max()
+    say(f"  {w.name}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert np.isfinite(o_g).all() and np.isfinite(l_g).all()
+    assert eo <= O_TOL, eo
+    assert el <= LSE_TOL, el
+
+
+# --------------------------------------------------------------- positions --
+
+@pytest.mark.parametrize("i", range(5))
+def test_position_ids_bit_exact(i):
+    w = make_workload(i)
+    say(f"positions: workload {w.name} T={w.total_tokens}")
+    L = layout_of(w)
+    pos = pg.pg_position_ids(L)
+    torch.cuda.synchronize()
+    ref = O.positions(oracle_layout(w))
+    assert np.array_equal(pos.cpu().numpy(), ref)
+
+
+def test_position_ids_edge_shapes():
+    for P, S in [([0, 7], [[4, 3], [5]]), ([6, 4, 3], [[], [0, 2], [0, 0]]), ([1], [[1, 1, 1]])]:
+        w = make_custom(P, S)
+        L = layout_of(w)
+        pos = pg.pg_position_ids(L)
+        assert np.array_equal(pos.cpu().numpy(), O.positions(oracle_layout(w)))
+
+
+# -------------------------------------------------------------------- RoPE --
+
+def _rope_compare(w, got, ref_f64):
+    if w.dtype == "bf16":
+        ref = O.round_to_bf16(ref_f64)
+        diff = np.abs(got.astype(np.float64) - ref)
+        ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
+        n_off = int((diff > 0).sum())
+        say(f"  rope {w.name}: {n_off} of {diff.size} elements differ by <= 1 ulp")
+        assert (diff <= ulp * 1.0000001).all()
+        assert n_off <= max(10, diff.size // 1000)
+    else:
+        assert np.abs(got.astype(np.float64) - ref_f64).max() <= 1e-6
+
+
+@pytest.mark.parametrize("i", range(5))
+def test_rope_against_oracle(i):
+    w, qkv = workload_inputs(i)
+    say(f"rope: workload {w.name}")
+    L = layout_of(w)
+    pos = pg.pg_position_ids(L)
+    q, k = to_dev(w, qkv["q"]), to_dev(w, qkv["k"])
+    qr, kr = pg.pg_rope(L, pos, q, k)
+    torch.cuda.synchronize()
+    lay = oracle_layout(w)
+    opos = O.positions(lay)
+    r = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([r.integers(0, w.total_tokens, size=512),
+                                     [0, w.total_tokens - 1, int(np.argmax(opos))]]))
+    q_h = host_vals(w, qkv["q"][toks])
+    k_h = host_vals(w, qkv["k"][toks])
+    _rope_compare(w, to_host_f32(qr[torch.from_numpy(toks).cuda()]), O.rope(q_h, opos[toks], w.rope_theta))
+    _rope_compare(w, to_host_f32(kr[torch.from_numpy(toks).cuda()]), O.rope(k_h, opos[toks], w.rope_theta))
+
+
+def test_rope_in_place_equals_out_of_place():
+    w, qkv = workload_inputs(1)
+    L = layout_of(w)
+    pos = pg.pg_position_ids(L)
+    q, k = to_dev(w, qkv["q"]), to_dev(w, qkv["k"])
+    qr, kr = pg.pg_rope(L, pos, q, k)
+    q2, k2 = q.clone(), k.clone()
+    pg.pg_rope(L, pos, q2, k2, q_out=q2, k_out=k2)
+    torch.cuda.synchronize()
+    assert torch.equal(q2.view(torch.int16), qr.view(torch.int16))
+    assert torch.equal(k2.view(torch.int16), kr.view(torch.int16))
+
+
+# --------------------------------------------------------------- attention --
+
+@pytest.mark.parametrize("i", range(5))
+def test_attention_against_oracle(i):
+    """pg_attn_fwd alone, fed exactly the oracle's Q/K/V."""
+    w, qkv = workload_inputs(i)
+    say(f"attn: workload {w.name} T={w.total_tokens} heads={w.num_q_heads}/{w.num_kv_heads}")
+    L = layout_of(w)
+    q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+    o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+    torch.cuda.synchronize()
+    lay = oracle_layout(w)
+    check_attn(w, o, lse, host_vals(w, qkv["q"]), host_vals(w, qkv["k"]),
+               host_vals(w, qkv["v"]), lay, full=(i <= 1))
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 4])
+def test_pipeline_against_oracle(i):
+    """positions -> RoPE -> attention, against the oracle pipeline (RoPE output
+    rounded to the storage dtype where the GPU hands it over)."""
+    w, qkv = workload_inputs(i)
+    say(f"pipeline: workload {w.name}")
+    L = layout_of(w)
+    pos = pg.pg_position_ids(L)
+    q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+    qr, kr = pg.pg_rope(L, pos, q, k)
+    o, lse = pg.pg_attn_fwd(L, qr, kr, v, w.softmax_scale)
+    torch.cuda.synchronize()
+    lay = oracle_layout(w)
+    opos = O.positions(lay)
+    qh, kh, vh = (host_vals(w, qkv[n]) for n in ("q", "k", "v"))
+    k_ref = O.storage_round(O.rope(kh, opos, w.rope_theta), w.dtype)
+    if i <= 1:
+        q_ref = O.storage_round(O.rope(qh, opos, w.rope_theta), w.dtype)
+        check_attn(w, o, lse, q_ref, k_ref, vh, lay, full=True)
+    else:
+        # roped Q only where sampled rows need it
+        toks, heads = sample_rows(lay, w.total_tokens, w.num_q_heads, 200, 99)
+        q_ref = np.zeros((w.total_tokens, w.num_q_heads, w.head_dim), dtype=np.float32)
+        q_ref[toks] = O.storage_round(O.rope(qh[toks], opos[toks], w.rope_theta), w.dtype)
+        o_ref, l_ref = O.attention_rows(q_ref, k_ref, vh, lay, w.softmax_scale, w.num_q_heads,
+                                        w.num_kv_heads, toks, heads)
+        o_g = to_host_f32(o)
+        l_g = lse.cpu().numpy()
+        eo = np.abs(o_g[toks, heads] - o_ref).max()
+        el = np.abs(l_g[heads, toks] - l_ref).max()
+        say(f"  {w.name}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+        assert eo <= O_TOL and el <= LSE_TOL
+
+
+EDGE = [
+    # prefix lens, suffix lens, (Hq, Hkv), d
+    ([0, 7], [[4, 3], [5]], (4, 1), 128),
+    ([6, 4, 3], [[], [0, 2], [0, 0]], (4, 1), 128),
+    ([1], [[1, 1, 1]], (8, 2), 128),
+    ([31, 33, 64], [[32, 1], [63, 65], [128, 129, 127]], (32, 8), 128),
+    ([65, 127, 129], [[64, 63], [1], [200, 0, 31]], (64, 8), 128),
+    ([300], [[1, 40, 0, 200, 33]], (2, 2), 128),
+    ([100, 0], [[70, 90], [33, 97]], (6, 2), 128),
+    ([45], [[19, 77, 3]], (3, 1), 128),
+    ([0], [[0, 130, 0]], (1, 1), 128),
+    ([200], [[]], (4, 4), 128),
+    ([37, 80], [[20, 9], [64]], (4, 2), 64),     # bf16, d = 64: per-row kernel
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_attention_edge_shapes(case):
+    P, S, (hq, hkv), d = EDGE[case]
+    w = make_custom(P, S, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seed=case)
+    say(f"attn edge case {case}: P={P} S={S} heads={hq}/{hkv} d={d}")
+    qkv = draw_qkv(w)
+    L = layout_of(w)
+    q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+    o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+    torch.cuda.synchronize()
+    if w.total_tokens == 0:
+        return
+    check_attn(w, o, lse, host_vals(w, qkv["q"]), host_vals(w, qkv["k"]),
+               host_vals(w, qkv["v"]), oracle_layout(w), full=True)
+
+
+def test_attention_fp32_edge_shapes():
+    for case, (P, S, (hq, hkv), d) in enumerate(EDGE[:4]):
+        w = make_custom(P, S, num_q_heads=hq, num_kv_heads=hkv, head_dim=64, dtype="f32",
+                        seed=case)
+        say(f"attn fp32 edge case {case}")
+        qkv = draw_qkv(w)
+        L = layout_of(w)
+        q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+        o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = O.attention(qkv["q"], qkv["k"], qkv["v"], oracle_layout(w),
+                                   w.softmax_scale, hq, hkv)
+        assert np.abs(o.cpu().numpy() - o_ref).max() <= 1e-5
+        assert np.abs(lse.cpu().numpy() - l_ref).max() <= 1e-5
+
+
+def test_empty_layout_launches_nothing():
+    w = make_custom([0, 0], [[0], []])
+    L = layout_of(w)
+    z = torch.empty((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    zk = torch.empty((0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = pg.pg_attn_fwd(L, z, zk, zk, 0.1)
+    pos = pg.pg_position_ids(L)
+    assert o.shape[0] == 0 and pos.shape[0] == 0
+
+
+# -------------------------------------------------------------- robustness --
+
+def test_deterministic_and_fully_written():
+    w, qkv = workload_inputs(1)
+    say("determinism / poison: workload dpo-bf16")
+    L = layout_of(w)
+    q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+    T, Hq, d = q.shape
+    o1 = torch.full_like(q, float("nan"))
+    l1 = torch.full((Hq, T), float("nan"), device="cuda")
+    pg.pg_attn_fwd(L, q, k, v, w.softmax_scale, o=o1, lse=l1)
+    o2 = torch.full_like(q, float("inf"))
+    l2 = torch.full((Hq, T), float("inf"), device="cuda")
+    pg.pg_attn_fwd(L, q, k, v, w.softmax_scale, o=o2, lse=l2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all() and torch.isfinite(l1).all()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_no_writes_past_outputs():
+    w, qkv = workload_inputs(1)
+    L = layout_of(w)
+    q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+    T, Hq, d = q.shape
+    pad = 4096
+    obuf = torch.full((T * Hq * d + pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((Hq * T + pad,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[:T * Hq * d].view(T, Hq, d)
+    lse = lbuf[:Hq * T].view(Hq, T)
+    pg.pg_attn_fwd(L, q, k, v, w.softmax_scale, o=o, lse=lse)
+    pos = torch.full((T + pad,), -3, dtype=torch.int64, device="cuda")
+    pg.pg_position_ids(L, pos=pos[:T])
+    torch.cuda.synchronize()
+    assert (obuf[T * Hq * d:] == 7.0).all() and (lbuf[Hq * T:] == 7.0).all()
+    assert (pos[T:] == -3).all()
+
+
+def test_packed_equals_unpacked_on_gpu():
+    """The same kernel on the unpacked layout (prefix duplicated per suffix)
+    gives the packed rows back: preference packing changes no result."""
+    from shared_prefix_packed_amd.baseline import unpacked_workload
+    w, qkv = workload_inputs(1)
+    say("packed vs unpacked on the GPU: workload dpo-bf16")
+    L = layout_of(w)
+    q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+    o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+    un = unpacked_workload(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    idx = torch.from_numpy(un.gather).cuda()
+    Lu = pg.pg_build_layout(un.prefix_lens, un.suffix_counts, un.suffix_lens, w.num_q_heads,
+                            w.num_kv_heads, w.head_dim, w.rope_theta)
+    ou, lu = pg.pg_attn_fwd(Lu, q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous(),
+                            w.softmax_scale)
+    torch.cuda.synchronize()
+    # every unpacked row maps to one packed row; compare all of them
+    d_o = (ou.float() - o[idx].float()).abs().max().item()
+    d_l = (lu - lse[:, idx]).abs().max().item()
+    say(f"  unpacked vs packed: max|dO|={d_o:.3e} max|dlse|={d_l:.3e}")
+    assert d_o <= 2 * O_TOL and d_l <= 2 * LSE_TOL

@@ -1,0 +1,212 @@
+"""CPU tests of libpg.so's host side: exported symbols, the layout builder
+against the oracle (bit-exact), work-list invariants and error paths.
+
+No compute entry point is called here (there is no GPU in this run)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import shared_prefix_packed_amd as pg
+from shared_prefix_packed_amd import _lib
+from conftest import ROOT, read_golden
+from oracle import pg_oracle as O
+from workloads import make_workload
+
+SHAPES = [
+    ([5, 9], [[3, 4], [2, 6, 1]]),
+    ([0, 7], [[4, 3], [5]]),
+    ([6, 4, 3], [[], [0, 2], [0, 0]]),
+    ([1], [[1, 1, 1]]),
+    ([31, 33, 64], [[32, 1], [63, 65], [128, 129, 127]]),
+    ([0], [[0, 3, 0]]),
+    ([17], [[]]),
+    ([300], [[1, 40, 0, 200, 33]]),
+    ([], []),
+    ([0, 0], [[0], []]),
+]
+
+
+def _flat(S):
+    return [len(s) for s in S], [x for s in S for x in s]
+
+
+def _build(P, S, hq=4, hkv=1, d=128, theta=1e4):
+    n, flat = _flat(S)
+    return pg.pg_build_layout_host(P, n, flat, hq, hkv, d, theta)
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "pg.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(pg_\w+)\s*\(", header, re.M))
+    assert {"pg_build_layout", "pg_position_ids", "pg_rope", "pg_attn_fwd"} <= declared
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_layout_bit_exact_against_oracle(shape):
+    P, S = shape
+    n, flat = _flat(S)
+    L = _build(P, S)
+    lay = O.layout(P, n, flat)
+    g, seg = L.offsets()
+    assert g.tolist() == lay["group_off"].tolist()
+    assert seg.tolist() == lay["seg_off"].tolist()
+    g0, pe, ss = L.tokens()
+    assert g0.tolist() == lay["g0"].tolist()
+    assert pe.tolist() == lay["pe"].tolist()
+    assert ss.tolist() == lay["ss"].tolist()
+    s = L.summary()
+    assert s.total_tokens == lay["total_tokens"]
+    assert s.useful_pairs == O.useful_pairs(lay)
+    assert s.unpacked_pairs == O.unpacked_pairs(lay)
+    pos = O.positions(lay)
+    assert s.max_position == (int(pos.max()) if pos.size else -1)
+    assert s.device_ready == 0
+
+
+def test_tiny_workload_against_hand_derivation():
+    gold = read_golden("tiny_layout.txt")
+    w = make_workload(0)
+    L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens, 1, 1, 64, 1e4)
+    g, seg = L.offsets()
+    assert g.tolist() == gold["group_off"] and seg.tolist() == gold["seg_off"]
+    assert L.summary().useful_pairs == gold["useful_pairs"][0]
+    assert L.summary().unpacked_pairs == gold["unpacked_pairs"][0]
+
+
+def _check_work_invariants(L, P, S, hq, hkv):
+    n, flat = _flat(S)
+    lay = O.layout(P, n, flat)
+    T = lay["total_tokens"]
+    items, spans = L.work()
+    s = L.summary()
+    hpw = s.heads_per_item
+    assert hpw == np.gcd(hq // hkv, 4)
+    assert s.block_tokens == 128 // hpw
+    cover = np.zeros((T, hq), dtype=np.int64)
+    total_cost = 0
+    for it in items:
+        t0, t1, hq0 = int(it["t0"]), int(it["t1"]), int(it["hq0"])
+        assert 0 < t1 - t0 <= s.block_tokens
+        assert int(lay["g0"][t0]) == int(lay["g0"][t1 - 1]), "item crosses a group"
+        assert it["pe"] == lay["pe"][t0]
+        assert (hq0 // (hq // hkv)) == ((hq0 + hpw - 1) // (hq // hkv)), "item mixes KV heads"
+        cover[t0:t1, hq0:hq0 + hpw] += 1
+        # spans: disjoint, ascending, inside the group; their union equals the
+        # union of the allowed keys of the item's tokens
+        sp = spans[it["span0"]:it["span0"] + it["nspan"]]
+        keys = set()
+        prev = -1
+        for k0, k1 in sp:
+            assert k0 < k1 and k0 >= prev
+            prev = k1
+            keys.update(range(k0, k1))
+        need = set()
+        pairs = 0
+        for t in range(t0, t1):
+            kt = O.allowed_keys(lay, t)
+            need.update(kt.tolist())
+            pairs += len(kt)
+        assert keys == need
+        assert it["cost"] == pairs * hpw and it["cost"] >= 1
+        total_cost += int(it["cost"])
+    assert (cover == 1).all(), "every (token, head) in exactly one item"
+    assert total_cost == O.useful_pairs(lay) * hq
+    costs = items["cost"]
+    assert (np.diff(costs) <= 0).all(), "launch order is cost-descending (LPT)"
+    assert s.max_item_cost == (int(costs.max()) if costs.size else 0)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("heads", [(4, 1), (32, 8), (64, 8), (2, 2), (6, 2), (3, 1)])
+def test_work_list_invariants(shape, heads):
+    P, S = shape
+    L = _build(P, S, hq=heads[0], hkv=heads[1])
+    _check_work_invariants(L, P, S, *heads)
+
+
+def test_work_list_on_dpo_workload():
+    w = make_workload(1)
+    L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens, 32, 8, 128, 5e5)
+    P = w.prefix_lens.tolist()
+    S = [s for _, s in w.groups()]
+    _check_work_invariants(L, P, S, 32, 8)
+
+
+def test_layouts_of_all_workloads_match_oracle_counts():
+    for i in range(5):
+        w = make_workload(i)
+        L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens,
+                                    w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta)
+        lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+        s = L.summary()
+        assert s.total_tokens == w.total_tokens
+        assert s.useful_pairs == O.useful_pairs(lay)
+        g, seg = L.offsets()
+        assert g.tolist() == lay["group_off"].tolist()
+        assert seg.tolist() == lay["seg_off"].tolist()
+        items, _ = L.work()
+        assert int(items["cost"].sum()) == O.useful_pairs(lay) * w.num_q_heads
+
+
+# ----------------------------------------------------------- error paths --
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except pg.PgError as e:
+        return e.status
+    return 0
+
+
+@pytest.mark.parametrize("args,status", [
+    (([5], [1], [-1], 4, 1, 128, 1e4), -1),       # negative suffix
+    (([-5], [1], [1], 4, 1, 128, 1e4), -1),       # negative prefix
+    (([5], [-1], [], 4, 1, 128, 1e4), -1),        # negative count
+    (([5], [1], [3], 6, 4, 128, 1e4), -1),        # Hq % Hkv != 0
+    (([5], [1], [3], 0, 1, 128, 1e4), -1),        # no heads
+    (([5], [1], [3], 4, 1, 96, 1e4), -2),         # unsupported head_dim
+    (([5], [1], [3], 4, 1, 128, 0.0), -1),        # theta
+    (([2**30, 2**30], [0, 0], [], 4, 1, 128, 1e4), -1),   # T >= 2^31
+])
+def test_invalid_arguments_are_reported(args, status):
+    assert _status(pg.pg_build_layout_host, *args) == status
+
+
+def test_null_pointers_are_reported():
+    lib = _lib.load()
+    out = ctypes.c_void_p()
+    P = (ctypes.c_int32 * 1)(3)
+    assert lib.pg_build_layout_host(1, None, P, None, 1, 1, 64, 1e4, ctypes.byref(out)) == -1
+    assert b"NULL" in lib.pg_last_error()
+    n = (ctypes.c_int32 * 1)(1)
+    assert lib.pg_build_layout_host(1, P, n, None, 1, 1, 64, 1e4, ctypes.byref(out)) == -1
+    assert lib.pg_build_layout_host(1, P, n, P, 1, 1, 64, 1e4, None) == -1
+    assert lib.pg_layout_info(None, None) == -1
+    assert lib.pg_position_ids(None, None, None) == -1
+    assert lib.pg_attn_fwd(None, None, None, None, None, None, 1, ctypes.c_float(1.0), None) == -1
+
+
+def test_compute_calls_need_an_uploaded_layout():
+    lib = _lib.load()
+    L = _build([5], [[3]])
+    dummy = ctypes.c_void_p(16)
+    assert lib.pg_position_ids(L.handle, dummy, None) == -5
+    assert lib.pg_rope(L.handle, dummy, dummy, dummy, dummy, dummy, 1, None) == -5
+    assert lib.pg_attn_fwd(L.handle, dummy, dummy, dummy, dummy, None, 1, ctypes.c_float(0.1), None) == -5
+    assert lib.pg_status_string(-5) == b"bad state"
+
+
+def test_empty_layout_is_a_no_op():
+    lib = _lib.load()
+    L = _build([], [])
+    s = L.summary()
+    assert s.total_tokens == 0 and s.num_items == 0 and s.max_position == -1
+    L2 = _build([0, 0], [[0], []])
+    assert L2.summary().total_tokens == 0
