@@ -117,6 +117,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-unpacked", action="store_true", help="skip the unpacked-layout baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes 5 times (calibrates "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against a known byte count)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -126,6 +129,15 @@ def main(argv=None):
 
     import numpy as np
     import torch
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 4 * n, "launches": 5}), flush=True)
+        return 0
     import shared_prefix_packed_amd as pg
     from shared_prefix_packed_amd.baseline import unpacked_workload
     from workloads import draw_qkv, make_workload, sha256

@@ -68,11 +68,15 @@ typedef struct pg_layout_summary {
   int64_t unpacked_pairs;  /* pairs of causal attention over every unpacked
                               prefix+suffix sequence (the work packing avoids)   */
   int64_t max_item_cost;   /* largest work item, in (query, key) pairs x heads   */
+  int64_t max_xcd_cost;    /* largest per-XCD sum of item costs (balance check)  */
 } pg_layout_summary;
 
 /* One work item of the attention launch: query tokens [t0, t1) of one group,
  * query heads [hq0, hq0 + heads_per_item), keys from spans
- * [span0, span0 + nspan) of the span list. Items are stored in launch order. */
+ * [span0, span0 + nspan) of the span list. Items are stored in launch order:
+ * item p runs on XCD p % 8; every item of one (group, KV head) sits on one
+ * XCD, and each XCD's items are in cost-descending order per cluster. Items
+ * with nspan == 0 are padding and do nothing. */
 typedef struct pg_work_item {
   int32_t t0;
   int32_t t1;

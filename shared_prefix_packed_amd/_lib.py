@@ -34,6 +34,7 @@ class LayoutSummary(ctypes.Structure):
         ("useful_pairs", c_int64),
         ("unpacked_pairs", c_int64),
         ("max_item_cost", c_int64),
+        ("max_xcd_cost", c_int64),
     ]
 
 

@@ -31,6 +31,8 @@
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int D = 128;
@@ -59,12 +61,16 @@ __device__ inline uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<cons
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  // nearest-even fp32 -> bf16 of two values (finite inputs)
-  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-  const uint32_t ra = (ua + 0x7fffu + ((ua >> 16) & 1u)) >> 16;
-  const uint32_t rb = (ub + 0x7fffu + ((ub >> 16) & 1u)) >> 16;
-  return ra | (rb << 16);
+  // nearest-even fp32 -> bf16 of two values in one v_cvt_pk_bf16_f32
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+
+// The running max is raised only when a tile's max exceeds it by more than
+// this many powers of two; until then exp2 arguments stay <= 8 and O, l are
+// not rescaled. The result is exact either way: numerator and denominator
+// share the same stale max.
+constexpr float RESCALE_SLACK = 8.0f;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -72,6 +78,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
   const pg_work_item it = a.items[blockIdx.x];
+  if (it.nspan == 0) return;   // padding of a shorter XCD queue
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -208,9 +215,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[1][i]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt * a.c_log2);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+      const float mt2 = mt * a.c_log2;
+      // rescale (wave-uniform decision) only when some row's max grew a lot
+      if (__ballot(mt2 > m_run + RESCALE_SLACK) != 0ull) {
+        const float m_new = fmaxf(m_run, mt2);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+      const float m_use = m_run;
       float lsum = 0.f;
       bf16x8_t pf[4];
 #pragma unroll
@@ -219,18 +236,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int i = 8 * (ks & 1) + 2 * jj;
-          const float p0 = fast_exp2(fmaf(sacc[ks >> 1][i], a.c_log2, -m_new));
-          const float p1 = fast_exp2(fmaf(sacc[ks >> 1][i + 1], a.c_log2, -m_new));
+          const float p0 = fast_exp2(fmaf(sacc[ks >> 1][i], a.c_log2, -m_use));
+          const float p1 = fast_exp2(fmaf(sacc[ks >> 1][i + 1], a.c_log2, -m_use));
           lsum += p0 + p1;
           (&pk.x)[jj] = pack_bf16x2(p0, p1);
         }
         pf[ks] = as_bf16x8(pk);
       }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      l_run += lsum;
       const unsigned char* vb = kb + K_BYTES;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {

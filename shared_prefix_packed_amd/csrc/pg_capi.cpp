@@ -170,6 +170,8 @@ pg_status pg_layout_info(const pg_layout* L, pg_layout_summary* info) {
   info->useful_pairs = L->useful_pairs;
   info->unpacked_pairs = L->unpacked_pairs;
   info->max_item_cost = L->max_item_cost;
+  info->max_xcd_cost = 0;
+  for (int64_t c : L->xcd_load) info->max_xcd_cost = c > info->max_xcd_cost ? c : info->max_xcd_cost;
   return PG_OK;
 }
 

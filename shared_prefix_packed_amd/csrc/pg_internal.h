@@ -30,6 +30,7 @@ struct pg_layout {
   std::vector<pg_work_item> items;
   std::vector<pg_key_span> spans;
   int64_t max_item_cost = 0;
+  std::vector<int64_t> xcd_load;   // summed item cost per XCD queue
 
   // device copy (one allocation, filled by pg_layout_upload)
   int device = -1;
@@ -69,3 +70,4 @@ hipError_t pg_launch_attn_mfma(const pg_layout& L, const void* q, const void* k,
 constexpr int PG_WAVE_QUERIES = 32;   // query tokens per wave in the MFMA kernel
 constexpr int PG_ITEM_WAVES = 4;      // waves per work item (workgroup)
 constexpr int PG_KEY_TILE = 64;       // keys per LDS tile
+constexpr int PG_XCDS = 8;            // XCDs of an MI355X; workgroup p runs on XCD p % 8

@@ -147,6 +147,7 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
     L.items.clear();
     L.spans.clear();
     L.max_item_cost = 0;
+    std::vector<int32_t> item_group;
     k = 0;
     int32_t seg = 0;   // index of the group's prefix segment in seg_off
     for (int32_t g = 0; g < num_groups; ++g) {
@@ -179,21 +180,68 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
             it.cost = pairs * hpw;
             L.max_item_cost = std::max(L.max_item_cost, it.cost);
             L.items.push_back(it);
+            item_group.push_back(g);
           }
         }
       }
       seg += 1 + nseg;
       k += nseg;
     }
-    // Longest-processing-time order: the dispatcher hands the next item to
-    // the first free slot, so cost-descending order is greedy LPT. Ties keep
-    // a fixed (t0, hq0) order so the list is deterministic.
-    std::stable_sort(L.items.begin(), L.items.end(),
-                     [](const pg_work_item& a, const pg_work_item& b) {
-                       if (a.cost != b.cost) return a.cost > b.cost;
-                       if (a.t0 != b.t0) return a.t0 < b.t0;
-                       return a.hq0 < b.hq0;
-                     });
+    // Launch order. Workgroups are dispatched round-robin over the XCDs
+    // (workgroup p runs on XCD p % 8), and each XCD has its own L2. All items
+    // of one (group, KV head) cluster read the same prefix K/V, so a cluster is
+    // placed on one XCD: clusters go to the XCD with the least load so far,
+    // largest first (LPT over cluster costs); inside an XCD, clusters run
+    // largest first and the items of a cluster largest first, so each XCD's
+    // own queue is in LPT order and the cluster's prefix stays hot in its L2.
+    // Positions of XCDs whose queue ran out are padded with empty items
+    // (nspan = 0), which the kernel leaves at once.
+    const int64_t ncl = int64_t(num_groups) * num_kv_heads;
+    std::vector<int64_t> cl_cost(static_cast<size_t>(ncl), 0);
+    std::vector<std::vector<int32_t>> cl_items(static_cast<size_t>(ncl));
+    for (size_t i = 0; i < L.items.size(); ++i) {
+      const pg_work_item& it = L.items[i];
+      const int64_t c = int64_t(item_group[i]) * num_kv_heads + it.hq0 / r;
+      cl_cost[size_t(c)] += it.cost;
+      cl_items[size_t(c)].push_back(int32_t(i));
+    }
+    std::vector<int64_t> order;
+    for (int64_t c = 0; c < ncl; ++c)
+      if (!cl_items[size_t(c)].empty()) order.push_back(c);
+    std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+      return cl_cost[size_t(a)] > cl_cost[size_t(b)];
+    });
+    std::vector<int64_t> xcd_load(PG_XCDS, 0);
+    std::vector<std::vector<int32_t>> xcd_queue(PG_XCDS);
+    for (int64_t c : order) {
+      int x = 0;
+      for (int j = 1; j < PG_XCDS; ++j)
+        if (xcd_load[j] < xcd_load[x]) x = j;
+      xcd_load[x] += cl_cost[size_t(c)];
+      std::vector<int32_t>& its = cl_items[size_t(c)];
+      std::stable_sort(its.begin(), its.end(), [&](int32_t a, int32_t b) {
+        const pg_work_item &ia = L.items[size_t(a)], &ib = L.items[size_t(b)];
+        if (ia.cost != ib.cost) return ia.cost > ib.cost;
+        if (ia.t0 != ib.t0) return ia.t0 < ib.t0;
+        return ia.hq0 < ib.hq0;
+      });
+      xcd_queue[x].insert(xcd_queue[x].end(), its.begin(), its.end());
+    }
+    size_t rows = 0;
+    for (const auto& qx : xcd_queue) rows = std::max(rows, qx.size());
+    std::vector<pg_work_item> launch;
+    launch.reserve(rows * PG_XCDS);
+    pg_work_item empty{};
+    empty.pe = 0;
+    empty.nspan = 0;
+    empty.cost = 0;
+    for (size_t i = 0; i < rows; ++i)
+      for (int x = 0; x < PG_XCDS; ++x)
+        launch.push_back(i < xcd_queue[x].size() ? L.items[size_t(xcd_queue[x][i])] : empty);
+    // drop trailing empty items
+    while (!launch.empty() && launch.back().nspan == 0) launch.pop_back();
+    L.items.swap(launch);
+    L.xcd_load = xcd_load;
   } catch (const std::bad_alloc&) {
     return pg_fail(PG_ERR_OOM, "host allocation failed");
   }

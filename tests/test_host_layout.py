@@ -80,23 +80,34 @@ def test_tiny_workload_against_hand_derivation():
     assert L.summary().unpacked_pairs == gold["unpacked_pairs"][0]
 
 
+XCDS = 8
+
+
 def _check_work_invariants(L, P, S, hq, hkv):
     n, flat = _flat(S)
     lay = O.layout(P, n, flat)
     T = lay["total_tokens"]
+    r = hq // hkv
     items, spans = L.work()
     s = L.summary()
     hpw = s.heads_per_item
-    assert hpw == np.gcd(hq // hkv, 4)
+    assert hpw == np.gcd(r, 4)
     assert s.block_tokens == 128 // hpw
     cover = np.zeros((T, hq), dtype=np.int64)
     total_cost = 0
-    for it in items:
+    xcd_of_cluster = {}
+    xcd_cost = np.zeros(XCDS, dtype=np.int64)
+    last = {}   # per XCD: (cluster, cost) of the previous real item
+    seen_done = set()
+    for p, it in enumerate(items):
+        if it["nspan"] == 0:
+            assert it["cost"] == 0 and it["t1"] == it["t0"]
+            continue
         t0, t1, hq0 = int(it["t0"]), int(it["t1"]), int(it["hq0"])
         assert 0 < t1 - t0 <= s.block_tokens
         assert int(lay["g0"][t0]) == int(lay["g0"][t1 - 1]), "item crosses a group"
         assert it["pe"] == lay["pe"][t0]
-        assert (hq0 // (hq // hkv)) == ((hq0 + hpw - 1) // (hq // hkv)), "item mixes KV heads"
+        assert hq0 // r == (hq0 + hpw - 1) // r, "item mixes KV heads"
         cover[t0:t1, hq0:hq0 + hpw] += 1
         # spans: disjoint, ascending, inside the group; their union equals the
         # union of the allowed keys of the item's tokens
@@ -116,11 +127,27 @@ def _check_work_invariants(L, P, S, hq, hkv):
         assert keys == need
         assert it["cost"] == pairs * hpw and it["cost"] >= 1
         total_cost += int(it["cost"])
+        # launch order: a (group, KV head) cluster lives on one XCD, runs as one
+        # contiguous stretch of that XCD's queue, cost-descending inside it
+        x = p % XCDS
+        cl = (int(lay["g0"][t0]), hq0 // r)
+        assert xcd_of_cluster.setdefault(cl, x) == x
+        xcd_cost[x] += int(it["cost"])
+        if x in last:
+            pcl, pcost = last[x]
+            if pcl == cl:
+                assert it["cost"] <= pcost
+            else:
+                assert cl not in seen_done, "cluster split in its XCD queue"
+                seen_done.add(pcl)
+        last[x] = (cl, int(it["cost"]))
     assert (cover == 1).all(), "every (token, head) in exactly one item"
     assert total_cost == O.useful_pairs(lay) * hq
-    costs = items["cost"]
-    assert (np.diff(costs) <= 0).all(), "launch order is cost-descending (LPT)"
-    assert s.max_item_cost == (int(costs.max()) if costs.size else 0)
+    real = items[items["nspan"] > 0]
+    assert s.max_item_cost == (int(real["cost"].max()) if real.size else 0)
+    assert s.max_xcd_cost == int(xcd_cost.max())
+    assert items.size == 0 or items[-1]["nspan"] > 0, "no trailing padding"
+    return xcd_cost
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -136,7 +163,22 @@ def test_work_list_on_dpo_workload():
     L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens, 32, 8, 128, 5e5)
     P = w.prefix_lens.tolist()
     S = [s for _, s in w.groups()]
-    _check_work_invariants(L, P, S, 32, 8)
+    cost = _check_work_invariants(L, P, S, 32, 8)
+    # LPT over 64 clusters: the heaviest XCD within 10 % of the mean
+    assert cost.max() <= 1.10 * cost.mean()
+
+
+@pytest.mark.parametrize("i", [2, 3, 4])
+def test_xcd_balance_of_large_workloads(i):
+    w = make_workload(i)
+    L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens,
+                                w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta)
+    items, _ = L.work()
+    real = items[items["nspan"] > 0]
+    mean = real["cost"].sum() / 8
+    assert L.summary().max_xcd_cost <= 1.10 * mean
+    # padding stays small next to the real items
+    assert (items["nspan"] == 0).sum() <= 0.25 * real.size
 
 
 def test_layouts_of_all_workloads_match_oracle_counts():
