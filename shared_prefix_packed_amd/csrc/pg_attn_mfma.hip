@@ -22,8 +22,9 @@
 //                                 S^T accumulators (no transpose needed)
 // V is transposed while it is staged into LDS; the key order inside each
 // 16-key step is permuted the same way for P and V, so every LDS read is one
-// 128-bit access. K rows are padded to 272 bytes and V^T rows are XOR-swizzled
-// in 16-byte chunks, which keeps reads and writes free of bank conflicts.
+// 128-bit access. K rows are padded to 272 bytes and the 16-byte chunks of V^T
+// row d are XOR-swizzled by (d >> 1) & 7, which keeps reads and writes free of
+// bank conflicts on the 64 four-byte banks of a gfx950 LDS.
 #include <hip/hip_runtime.h>
 
 #include "pg_internal.h"
@@ -73,6 +74,12 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 constexpr float RESCALE_SLACK = 8.0f;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields left at "no wait").
+// Issued once before the tile loop so every load made before it is known to
+// have landed; otherwise the loop's wait counters also cover those loads and
+// each tile would wait for the next tile's prefetch as well.
+__device__ inline void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
@@ -147,8 +154,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       const int d0 = 8 * vc + 2 * m;
       const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
       const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u));
-      *reinterpret_cast<uint2*>(vb + d0 * 128 + 16 * (v_cl ^ ((2 * m) & 7)) + 8 * v_hb) = lo;
-      *reinterpret_cast<uint2*>(vb + (d0 + 1) * 128 + 16 * (v_cl ^ ((2 * m + 1) & 7)) + 8 * v_hb) = hi;
+      const int sw = (d0 >> 1) & 7;   // same swizzle for rows d0 and d0 + 1
+      *reinterpret_cast<uint2*>(vb + d0 * 128 + 16 * (v_cl ^ sw) + 8 * v_hb) = lo;
+      *reinterpret_cast<uint2*>(vb + (d0 + 1) * 128 + 16 * (v_cl ^ sw) + 8 * v_hb) = hi;
     }
   };
 
@@ -157,6 +165,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   pg_key_span sp = a.spans[s];
   int ka = sp.k0;
   gload(ka, sp.k1);
+  wait_all_vmem();
   lstore(0);
   __syncthreads();
   int buf = 0;
@@ -199,14 +208,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       }
       // S^T C-layout: register i of block kb2 holds key 32 kb2 + 8 (i/4) + 4 half + i%4.
       if (!full) {
-        const int k1 = sp.k1;
+        // allowed keys of this lane's query inside the span: [lo, hi] with
+        // lo = own segment start (suffix spans) and hi = min(t, k1 - 1); in
+        // tile-local offsets c = 32 kb + 8 (i/4) + i%4 after removing 4 half.
+        const int base = ka + 4 * half;
+        const int lo = (is_prefix ? ka : ss_t) - base;
+        const int hi = min(tq, sp.k1 - 1) - base;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int j = ka + 32 * kb2 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool ok = (j < k1) && (j <= tq) && (is_prefix || j >= ss_t);
-            sacc[kb2][i] = ok ? sacc[kb2][i] : -__builtin_inff();
+            const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+            sacc[kb2][i] = (c >= lo && c <= hi) ? sacc[kb2][i] : -__builtin_inff();
           }
       }
       float mt = sacc[0][0];
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(
-              vb + (32 * db + qi) * 128 + 16 * ((2 * ks + half) ^ (qi & 7))));
+              vb + (32 * db + qi) * 128 + 16 * ((2 * ks + half) ^ ((qi >> 1) & 7))));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks], acc[db], 0, 0, 0);
         }
       }
