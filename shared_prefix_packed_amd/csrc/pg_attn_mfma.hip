@@ -36,6 +36,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+
 constexpr int D = 128;
 constexpr int KT = PG_KEY_TILE;         // 64 keys per tile
 constexpr int QW = PG_WAVE_QUERIES;     // 32 queries per wave
@@ -58,6 +59,16 @@ struct MfmaArgs {
 };
 
 __device__ inline uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 dword3: untyped
+// 32-bit data format). A load whose offset lies at or past `bytes` returns
+// zeros, so rows past the end of a key span need no clamping.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ inline uint4 buf16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -88,12 +99,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   if (it.nspan == 0) return;   // padding of a shorter XCD queue
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int qi = lane & 31;     // query column of this lane inside the wave
   const int half = lane >> 5;   // which half of each 16-wide k step the lane feeds
 
   const int h = it.hq0 + wave % a.hpw;
-  const int hk = h / a.r;
+  const int hk = it.hq0 / a.r;   // one KV head per item
   const int tb = it.t0 + QW * (wave / a.hpw);
   const int te = min(tb + QW, it.t1);
   const bool wave_active = tb < te;
@@ -122,22 +133,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
 
   // Staging roles. K: 16 lanes per 256-byte row, rows kr + 16 i.
   // V: lane takes keys 4 va .. 4 va + 3 and d = 8 vc .. 8 vc + 7.
+  // Per-lane byte offsets from the tile's first row are fixed; only the
+  // scalar base of the buffer resource moves from tile to tile.
   const int kc = tid & 15, kr = tid >> 4;
   const int va = tid & 15, vc = tid >> 4;
-  const int64_t tok_stride = int64_t(a.Hkv) * D;
-  const uint16_t* kbase = a.k + int64_t(hk) * D + 8 * kc;
-  const uint16_t* vbase = a.v + int64_t(hk) * D + 8 * vc;
+  const int row_bytes = a.Hkv * D * 2;
+  int koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = (kr + 16 * i) * row_bytes + 16 * kc;
+    voff[i] = (4 * va + i) * row_bytes + 16 * vc;
+  }
+  const uint16_t* kbase = a.k + int64_t(hk) * D;
+  const uint16_t* vbase = a.v + int64_t(hk) * D;
   const int v_cl = 2 * (va >> 2) + (va & 1);   // logical 16-byte chunk of keys 4va..4va+3
   const int v_hb = (va >> 1) & 1;              // which 8-byte half of that chunk
   uint4 rk[4], rv[4];
 
   auto gload = [&](int ka, int k1) {
+    // valid bytes: rows ka .. k1-1, 256 bytes of head hk in the last one
+    const int bytes = (k1 - ka - 1) * row_bytes + D * 2;
+    const int64_t off = int64_t(ka) * a.Hkv * D;
+    const __amdgpu_buffer_rsrc_t rsk = make_rsrc(kbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rsv = make_rsrc(vbase + off, bytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rowk = min(ka + kr + 16 * i, k1 - 1);
-      rk[i] = ldg16(kbase + int64_t(rowk) * tok_stride);
-      const int rowv = min(ka + 4 * va + i, k1 - 1);
-      rv[i] = ldg16(vbase + int64_t(rowv) * tok_stride);
+      rk[i] = buf16(rsk, koff[i]);
+      rv[i] = buf16(rsv, voff[i]);
     }
   };
   auto lstore = [&](int buf) {
@@ -208,6 +230,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       }
       // S^T C-layout: register i of block kb2 holds key 32 kb2 + 8 (i/4) + 4 half + i%4.
       if (!full) {
+        // (the empty volatile asm keeps this a real, uniform branch: without
+        // it the compiler turns the mask into selects executed on every tile)
+        asm volatile("" ::: "memory");
         // allowed keys of this lane's query inside the span: [lo, hi] with
         // lo = own segment start (suffix spans) and hi = min(t, k1 - 1); in
         // tile-local offsets c = 32 kb + 8 (i/4) + i%4 after removing 4 half.
@@ -251,6 +276,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
           const int i = 8 * (ks & 1) + 2 * jj;
           const float p0 = fast_exp2(fmaf(sacc[ks >> 1][i], a.c_log2, -m_use));
           const float p1 = fast_exp2(fmaf(sacc[ks >> 1][i + 1], a.c_log2, -m_use));
+          // the denominator sums the unrounded p in fp32: a sum of the bf16 P
+          // would carry bf16's 2^-9 relative error into lse
           lsum += p0 + p1;
           (&pk.x)[jj] = pack_bf16x2(p0, p1);
         }
