@@ -8,23 +8,36 @@
 // diagram). Tiles are built over the packed query-key region and fully masked
 // tiles are never visited ("PackInfer", abstract).
 //
-// Work item (one workgroup of 4 waves): query tokens [t0, t1) of one group and
+// Work item (one workgroup of 8 waves): query tokens [t0, t1) of one group and
 // `hpw` query heads of one KV head; wave w takes head hq0 + w % hpw and the
-// 32-token block w / hpw. All waves share every K/V tile staged in LDS, so a
-// tile fetched once serves hpw heads (GQA) and every suffix in the block (the
-// prefix keys are common to all of them).
+// 32-token block w / hpw. All eight waves share every K/V tile staged in LDS,
+// so a tile fetched once serves hpw heads (GQA) and every suffix in the block
+// (the prefix keys are common to all of them).
 //
 // Per wave and 64-key tile, with 32x32x16 bf16 MFMAs:
 //   S^T[key][query] = K . Q^T     A = K rows from LDS, B = Q from registers
 //   online softmax per query      one query per lane, keys split over the two
-//                                 lane halves: 31 in-lane max/add + 1 swap
-//   O^T[d][query]  += V^T . P^T   A = V^T from LDS, B = P straight from the
-//                                 S^T accumulators (no transpose needed)
-// V is transposed while it is staged into LDS; the key order inside each
-// 16-key step is permuted the same way for P and V, so every LDS read is one
-// 128-bit access. K rows are padded to 272 bytes and the 16-byte chunks of V^T
-// row d are XOR-swizzled by (d >> 1) & 7, which keeps reads and writes free of
-// bank conflicts on the 64 four-byte banks of a gfx950 LDS.
+//                                 lane halves: in-lane max/add + 1 shuffle
+//   O^T[d][query]  += V^T . P^T   A = V^T via transposing LDS reads, B = P
+//                                 straight from the S^T accumulators
+//
+// Ping-pong schedule. Softmax costs about as many VALU cycles (one quarter-rate
+// exp per score) as the two products cost MFMA cycles, so the two must run at
+// the same time. Each wave alternates an MFMA step (PV of the previous tile,
+// then S of the current one) with a VALU step (softmax of the current tile).
+// Waves 0-3 (group A) and 4-7 (group B) are one step apart and every step ends
+// in a workgroup barrier. Waves w and w + 4 share a SIMD, so on each SIMD one
+// wave feeds the matrix cores while the other runs the softmax.
+//
+// Staging. K and V tiles go from global memory straight into a four-stage LDS
+// ring (buffer loads that write LDS, no registers), issued two tiles ahead:
+// group A fetches K, group B fetches V. K rows keep their 256 bytes with the
+// 16-byte chunks XOR-swizzled by row (conflict-free 128-bit reads). V is stored
+// in the order the transposing read ds_read_b64_tr_b16 consumes it: for each
+// 16-key step, 8-key half and 32-d block one 512-byte block, in which lane s of
+// every 16-lane group owns 8 bytes; one such read then hands each lane 4 keys
+// of one d, which is exactly an MFMA A-operand fragment of V^T. The key order
+// inside each 16-key step is the one the S^T accumulators give P.
 #include <hip/hip_runtime.h>
 
 #include "pg_internal.h"
@@ -32,18 +45,22 @@
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int D = 128;
 constexpr int KT = PG_KEY_TILE;         // 64 keys per tile
 constexpr int QW = PG_WAVE_QUERIES;     // 32 queries per wave
-constexpr int K_PITCH = 272;            // bytes per K row in LDS (256 + 16 pad)
-constexpr int K_BYTES = KT * K_PITCH;   // 17408
-constexpr int V_BYTES = D * KT * 2;     // 16384: V^T, 128 bytes per d row
+constexpr int NWAVES = PG_ITEM_WAVES;   // 8 waves: two groups of 4
+constexpr int K_BYTES = KT * D * 2;     // 16384: 64 rows x 256 bytes, swizzled chunks
+constexpr int V_BYTES = KT * D * 2;     // 16384: 32 blocks of 512 bytes
 constexpr int STAGE = K_BYTES + V_BYTES;
+constexpr int NSTAGE = 4;
+constexpr int LOADS_PER_TILE = 4;       // 1 KB buffer->LDS loads per wave per tile
 
 struct MfmaArgs {
   const uint16_t* q;
@@ -60,17 +77,46 @@ struct MfmaArgs {
 
 __device__ inline uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Raw buffer resource over `bytes` bytes from `base` (gfx9 dword3: untyped
-// 32-bit data format). A load whose offset lies at or past `bytes` returns
-// zeros, so rows past the end of a key span need no clamping.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (four SGPRs) over `bytes` bytes from `base`: 48-bit base,
+// stride 0, num_records = bytes, gfx9 dword3 = untyped 32-bit data. Loads at
+// or past `bytes` return zeros, so rows past the end of a key span need no
+// clamping. Every field must be wave-uniform.
+__device__ inline i32x4_t make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(p)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
 }
-__device__ inline uint4 buf16(__amdgpu_buffer_rsrc_t r, int voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+
+// 16 bytes per lane from buffer `r` at byte offset `voff` straight into LDS at
+// byte address lds + 16 * lane (lds is wave-uniform). Written as asm so the
+// compiler does not guard every later LDS read with a full vmcnt(0) wait: the
+// loads only write LDS (no VGPR result), and their completion is awaited
+// explicitly (wait_vmem_*) before the barrier that publishes the tile. M0 is
+// written here; the compiler keeps no value in M0 across this kernel's code
+// (no M0-relative LDS instruction is used, checked in the generated code).
+__device__ inline void buf16_to_lds(i32x4_t r, int voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(lds)
+      : "memory");
 }
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Transposing LDS read: inside each group of 16 lanes, lane d receives element
+// d % 4 of the 8-byte chunks addressed by lanes 4 j + d / 4, j = 0..3.
+__device__ inline i16x4_t lds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+}
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   // nearest-even fp32 -> bf16 of two values in one v_cvt_pk_bf16_f32
@@ -86,20 +132,78 @@ constexpr float RESCALE_SLACK = 8.0f;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields left at "no wait").
-// Issued once before the tile loop so every load made before it is known to
-// have landed; otherwise the loop's wait counters also cover those loads and
-// each tile would wait for the next tile's prefetch as well.
-__device__ inline void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (gfx9 encoding: expcnt and lgkmcnt fields left at "no wait").
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ inline void wait_vmem_but_one_tile() { __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE); }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+// End of a ping-pong step: this wave's LDS accesses done, then the workgroup
+// barrier. Global loads stay in flight across it (a __syncthreads() fence would
+// drain them). The asm's memory clobber keeps the compiler from moving memory
+// operations across; the scheduling barriers keep arithmetic on its side.
+__device__ inline void step_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scheduling pattern for a block of NM MFMAs fed by LDS reads: AHEAD reads
+// first, then PER reads after each MFMA until the reads run out.
+template <int I, int NM, int PER, int REST>
+__device__ inline void sched_mfma_then_reads() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    constexpr int r = REST >= PER ? PER : REST;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);   // r LDS reads
+    sched_mfma_then_reads<I + 1, NM, PER, REST - r>();
+  }
+}
+template <int AHEAD, int PER, int NM>
+__device__ inline void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+  sched_mfma_then_reads<0, NM, PER, NM * PER - AHEAD>();
+}
+
+// Walks the 64-key tiles of an item's key spans (all scalar state).
+struct TileIter {
+  int s, s_end, ka;
+  pg_key_span sp;
+  // (readfirstlane: keep the state in SGPRs, so spans are read with scalar
+  // loads that never wait behind the in-flight tile fetches)
+  __device__ void load(const pg_key_span* spans) {
+    // the span table is read-only for the kernel: read it through the constant
+    // address space so these are scalar loads (lgkmcnt), not vector loads whose
+    // vmcnt wait would also drain the tile fetches in flight
+    const __attribute__((address_space(4))) int* cs =
+        (const __attribute__((address_space(4))) int*)(spans);
+    const int idx = 2 * __builtin_amdgcn_readfirstlane(s);
+    sp.k0 = __builtin_amdgcn_readfirstlane(cs[idx]);
+    sp.k1 = __builtin_amdgcn_readfirstlane(cs[idx + 1]);
+    ka = sp.k0;
+  }
+  __device__ void init(const pg_key_span* spans, int s0, int n) {
+    s = __builtin_amdgcn_readfirstlane(s0);
+    s_end = __builtin_amdgcn_readfirstlane(s0 + n);
+    load(spans);
+  }
+  __device__ void next(const pg_key_span* spans) {
+    ka += KT;
+    if (ka >= sp.k1) {
+      ++s;
+      if (s < s_end) load(spans);
+    }
+  }
+};
+
+__global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
 
   const pg_work_item it = a.items[blockIdx.x];
   if (it.nspan == 0) return;   // padding of a shorter XCD queue
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int grp = wave >> 2;    // 0: group A, 1: group B (one step later)
+  const int wg = wave & 3;      // wave inside its group
   const int qi = lane & 31;     // query column of this lane inside the wave
   const int half = lane >> 5;   // which half of each 16-wide k step the lane feeds
 
@@ -110,6 +214,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   const bool wave_active = tb < te;
   const int tq = wave_active ? min(tb + qi, te - 1) : it.t0;   // padded rows repeat the last one
   const bool row_valid = wave_active && (tb + qi < te);
+
+  // Masked keys get p = 0, which multiplies V: V slots must never hold a NaN
+  // pattern, so the V half of every stage starts out zero.
+  for (int i = tid; i < NSTAGE * V_BYTES / 16; i += 64 * NWAVES) {
+    const int st = i / (V_BYTES / 16), o = i % (V_BYTES / 16);
+    *reinterpret_cast<uint4*>(smem + st * STAGE + K_BYTES + 16 * o) = make_uint4(0, 0, 0, 0);
+  }
 
   // Q as the B operand of S^T = K Q^T: lane holds d = 16 ks + 8 half + 0..7.
   bf16x8_t qf[8];
@@ -131,114 +242,165 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   float m_run = -1.0e30f;   // finite start: exp2(m_run - m_new) is 0, never NaN
   float l_run = 0.f;
 
-  // Staging roles. K: 16 lanes per 256-byte row, rows kr + 16 i.
-  // V: lane takes keys 4 va .. 4 va + 3 and d = 8 vc .. 8 vc + 7.
-  // Per-lane byte offsets from the tile's first row are fixed; only the
-  // scalar base of the buffer resource moves from tile to tile.
-  const int kc = tid & 15, kr = tid >> 4;
-  const int va = tid & 15, vc = tid >> 4;
-  const int row_bytes = a.Hkv * D * 2;
-  int koff[4], voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    koff[i] = (kr + 16 * i) * row_bytes + 16 * kc;
-    voff[i] = (4 * va + i) * row_bytes + 16 * vc;
+  // number of tiles of this item
+  int ntiles = 0;
+  for (int s = it.span0; s < it.span0 + it.nspan; ++s) {
+    const pg_key_span sp = a.spans[s];
+    ntiles += (sp.k1 - sp.k0 + KT - 1) / KT;
   }
-  const uint16_t* kbase = a.k + int64_t(hk) * D;
-  const uint16_t* vbase = a.v + int64_t(hk) * D;
-  const int v_cl = 2 * (va >> 2) + (va & 1);   // logical 16-byte chunk of keys 4va..4va+3
-  const int v_hb = (va >> 1) & 1;              // which 8-byte half of that chunk
-  uint4 rk[4], rv[4];
 
-  auto gload = [&](int ka, int k1) {
+  // ---- staging: per-lane global byte offsets from a tile's first key row ----
+  // Wave wg of a group writes LDS blocks 4 wg + i (i = 0..3) of 1 KB each.
+  // K block b = rows 4b..4b+3: lane L -> row 4b + L/16, stored chunk L%16,
+  //   which holds global chunk (L%16) ^ (row & 15).
+  // V block b = 512-byte read blocks 2b, 2b+1 (block index ks*8 + rd*4 + db);
+  //   16-byte unit u of a read block holds V[16ks + 8rd + 4(u/16) + (u%8)/2]
+  //   [32db + 16((u/8)&1) + 8(u&1) .. +8].
+  const int row_bytes = a.Hkv * D * 2;
+  int goff[LOADS_PER_TILE];
+#pragma unroll
+  for (int i = 0; i < LOADS_PER_TILE; ++i) {
+    const int b = 4 * wg + i;
+    if (grp == 0) {
+      const int row = 4 * b + (lane >> 4);
+      const int chunk = (lane & 15) ^ (row & 15);
+      goff[i] = row * row_bytes + 16 * chunk;
+    } else {
+      const int rb = 2 * b + (lane >> 5);   // 512-byte read block
+      const int ks = rb >> 3, rd = (rb >> 2) & 1, db = rb & 3;
+      const int u = lane & 31, g = u >> 3;
+      const int key = 16 * ks + 8 * rd + 4 * (g >> 1) + ((u & 7) >> 1);
+      const int d0 = 32 * db + 16 * (g & 1) + 8 * (u & 1);
+      goff[i] = key * row_bytes + 2 * d0;
+    }
+  }
+  const uint16_t* gbase = (grp == 0 ? a.k : a.v) + int64_t(hk) * D;
+  const int region = grp == 0 ? 0 : K_BYTES;
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
+
+  auto gload = [&](int ka, int k1, int stage) {
+    // tile bounds are wave-uniform; say so, or the resource build turns into
+    // a per-lane loop around every load
+    ka = __builtin_amdgcn_readfirstlane(ka);
+    k1 = __builtin_amdgcn_readfirstlane(k1);
     // valid bytes: rows ka .. k1-1, 256 bytes of head hk in the last one
     const int bytes = (k1 - ka - 1) * row_bytes + D * 2;
-    const int64_t off = int64_t(ka) * a.Hkv * D;
-    const __amdgpu_buffer_rsrc_t rsk = make_rsrc(kbase + off, bytes);
-    const __amdgpu_buffer_rsrc_t rsv = make_rsrc(vbase + off, bytes);
+    const i32x4_t rs = make_rsrc(gbase + int64_t(ka) * a.Hkv * D, bytes);
+    const uint32_t dst = lds_base + uint32_t(stage * STAGE + region + 4096 * wg);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rk[i] = buf16(rsk, koff[i]);
-      rv[i] = buf16(rsv, voff[i]);
-    }
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* kb = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(kb + (kr + 16 * i) * K_PITCH + 16 * kc) = rk[i];
-    unsigned char* vb = kb + K_BYTES;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t x0 = (&rv[0].x)[m], x1 = (&rv[1].x)[m];
-      const uint32_t x2 = (&rv[2].x)[m], x3 = (&rv[3].x)[m];
-      // d = 8 vc + 2m (low halves) and d + 1 (high halves); 4 keys each
-      const int d0 = 8 * vc + 2 * m;
-      const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
-      const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u));
-      const int sw = (d0 >> 1) & 7;   // same swizzle for rows d0 and d0 + 1
-      *reinterpret_cast<uint2*>(vb + d0 * 128 + 16 * (v_cl ^ sw) + 8 * v_hb) = lo;
-      *reinterpret_cast<uint2*>(vb + (d0 + 1) * 128 + 16 * (v_cl ^ sw) + 8 * v_hb) = hi;
-    }
+    for (int i = 0; i < LOADS_PER_TILE; ++i) buf16_to_lds(rs, goff[i], dst + 1024 * i);
   };
 
-  int s = it.span0;
-  const int s_end = it.span0 + it.nspan;
-  pg_key_span sp = a.spans[s];
-  int ka = sp.k0;
-  gload(ka, sp.k1);
-  wait_all_vmem();
-  lstore(0);
+  // ---- LDS read offsets --------------------------------------------------
+  // S: A operand of block kb, k step ks = K row 32 kb + qi, chunk 2 ks + half,
+  //    stored at chunk (2 ks + half) ^ (qi & 15).
+  int koff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * 256 + 16 * ((2 * ks + half) ^ (qi & 15));
+  // PV: lane reads 8 bytes at 8 * lane of each 512-byte block.
+  const int voff = K_BYTES + 8 * lane;
+
+  // Prologue: tiles 0 and 1 (K by group A, V by group B) into stages 0 and 1.
+  TileIter ld;
+  ld.init(a.spans, it.span0, it.nspan);
+  gload(ld.ka, ld.sp.k1, 0);
+  ld.next(a.spans);
+  if (ntiles > 1) {
+    gload(ld.ka, ld.sp.k1, 1);
+    ld.next(a.spans);
+  }
+  wait_vmem_all();
   __syncthreads();
-  int buf = 0;
 
-  while (true) {
-    // next tile
-    int ns = s, nka = ka + KT;
-    pg_key_span nsp = sp;
-    if (nka >= sp.k1) {
-      ns = s + 1;
-      if (ns < s_end) {
-        nsp = a.spans[ns];
-        nka = nsp.k0;
-      }
-    }
-    const bool has_next = ns < s_end;
-    if (has_next) gload(nka, nsp.k1);
+  TileIter cp;   // tile of the next S product
+  cp.init(a.spans, it.span0, it.nspan);
+  f32x16_t sacc[2];
+  bf16x8_t pf[4];
+  bool s_part = false;   // this wave computed S of the tile now in sacc
+  bool p_part = false;   // this wave holds P of the tile awaiting PV
+  int v_ka = 0, v_k1 = 0;
+  bool v_prefix = true, v_full = true;
 
-    // ---- compute on the current tile ------------------------------------
-    const bool is_prefix = sp.k1 <= it.pe;
-    bool part = wave_active && ka <= te - 1;
-    if (!is_prefix) part = part && (__ballot(row_valid && ss_t == sp.k0) != 0ull);
-    if (part) {
-      const bool full = (ka + KT <= sp.k1) && (ka + KT - 1 <= tb) && (is_prefix || ss_max <= ka);
-      const unsigned char* kb = smem + buf * STAGE;
-      f32x16_t sacc[2];
+  // One MFMA step (n) and one VALU step (softmax of tile n), as lambdas; group
+  // A runs [M(n); V(n)] and group B [V(n-1); M(n)], so that across a loop back
+  // edge only P (group A) or only the S accumulators (group B) stay live.
+  auto mfma_step = [&](const int n) {
+    // MFMA step n: PV(n-1), S(n), then fetch tile n+2
+    __builtin_amdgcn_s_setprio(1);
+    if (p_part) {
+      const unsigned char* vb = smem + ((n - 1) % NSTAGE) * STAGE + voff;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[0][i] = 0.f;
-        sacc[1][i] = 0.f;
-      }
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const bf16x8_t av = as_bf16x8(
-              *reinterpret_cast<const uint4*>(kb + (32 * kb2 + qi) * K_PITCH + 32 * ks + 16 * half));
-          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[kb2], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) {
+          const i16x4_t lo = lds_read_tr(vb + 512 * (8 * ks + db));
+          const i16x4_t hi = lds_read_tr(vb + 512 * (8 * ks + 4 + db));
+          const bf16x8_t av = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks], acc[db], 0, 0, 0);
         }
       }
-      // S^T C-layout: register i of block kb2 holds key 32 kb2 + 8 (i/4) + 4 half + i%4.
-      if (!full) {
-        // (the empty volatile asm keeps this a real, uniform branch: without
-        // it the compiler turns the mask into selects executed on every tile)
+      // issue order: 6 reads ahead, then (1 MFMA, 2 reads), so LDS latency
+      // hides behind the matrix core instead of stalling it
+      sched_reads_ahead<6, 2, 16>();
+    }
+    // keep PV(n-1) ahead of S(n): P dies before the S accumulators are born
+    __builtin_amdgcn_sched_barrier(0);
+    s_part = false;
+    if (n < ntiles) {
+      const int ka = cp.ka;
+      const pg_key_span sp = cp.sp;
+      const bool is_prefix = sp.k1 <= it.pe;
+      bool part = wave_active && ka <= te - 1;
+      if (!is_prefix) part = part && (__ballot(row_valid && ss_t == sp.k0) != 0ull);
+      v_ka = ka;
+      v_k1 = sp.k1;
+      v_prefix = is_prefix;
+      v_full = (ka + KT <= sp.k1) && (ka + KT - 1 <= tb) && (is_prefix || ss_max <= ka);
+      s_part = part;
+      if (part) {
+        const unsigned char* kb = smem + (n % NSTAGE) * STAGE;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[0][i] = 0.f;
+          sacc[1][i] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const bf16x8_t av =
+                as_bf16x8(*reinterpret_cast<const uint4*>(kb + 8192 * kb2 + koff[ks]));
+            sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[kb2], 0, 0, 0);
+          }
+        }
+        sched_reads_ahead<4, 1, 16>();
+      }
+      cp.next(a.spans);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Tile n+2 replaces tile n-2 in the ring; its last reader (PV(n-2) of
+    // group B) finished before the previous barrier.
+    if (n + 2 < ntiles) {
+      gload(ld.ka, ld.sp.k1, (n + 2) % NSTAGE);
+      ld.next(a.spans);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto valu_step = [&](const int n) {
+    // VALU step: softmax of tile n (in sacc) -> P
+    p_part = s_part;
+    if (s_part) {
+      // S^T C-layout: register i of block kb holds key 32 kb + 8 (i/4) + 4 half + i%4.
+      if (!v_full) {
+        // (the empty volatile asm keeps this a real, uniform branch)
         asm volatile("" ::: "memory");
         // allowed keys of this lane's query inside the span: [lo, hi] with
         // lo = own segment start (suffix spans) and hi = min(t, k1 - 1); in
         // tile-local offsets c = 32 kb + 8 (i/4) + i%4 after removing 4 half.
-        const int base = ka + 4 * half;
-        const int lo = (is_prefix ? ka : ss_t) - base;
-        const int hi = min(tq, sp.k1 - 1) - base;
+        const int base = v_ka + 4 * half;
+        const int lo = (v_prefix ? v_ka : ss_t) - base;
+        const int hi = min(tq, v_k1 - 1) - base;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -267,7 +429,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       }
       const float m_use = m_run;
       float lsum = 0.f;
-      bf16x8_t pf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         uint4 pk;
@@ -284,25 +445,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
         pf[ks] = as_bf16x8(pk);
       }
       l_run += lsum;
-      const unsigned char* vb = kb + K_BYTES;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(
-              vb + (32 * db + qi) * 128 + 16 * ((2 * ks + half) ^ ((qi >> 1) & 7))));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks], acc[db], 0, 0, 0);
-        }
-      }
     }
+    s_part = false;
+    // Tile n+1 (fetched by this group in M(n-1)) must have landed before the
+    // barrier: it is read from the next step on. The fetch of tile n+2 (issued
+    // in M(n), if that tile exists) may stay in flight.
+    if (n + 2 < ntiles)
+      wait_vmem_but_one_tile();
+    else
+      wait_vmem_all();
+  };
 
-    if (!has_next) break;
-    lstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    s = ns;
-    ka = nka;
-    sp = nsp;
+  if (grp == 0) {
+    for (int n = 0; n <= ntiles; ++n) {
+      mfma_step(n);
+      step_barrier();
+      valu_step(n);
+      step_barrier();
+    }
+  } else {
+    for (int n = 0; n <= ntiles; ++n) {
+      valu_step(n - 1);
+      step_barrier();
+      mfma_step(n);
+      step_barrier();
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -345,6 +512,6 @@ hipError_t pg_launch_attn_mfma(const pg_layout& L, const void* q, const void* k,
   a.r = L.Hq / L.Hkv;
   a.hpw = L.heads_per_item;
   a.c_log2 = softmax_scale * 1.44269504088896340736f;
-  attn_fwd_bf16_d128<<<dim3(uint32_t(L.items.size())), dim3(256), 0, stream>>>(a);
+  attn_fwd_bf16_d128<<<dim3(uint32_t(L.items.size())), dim3(64 * NWAVES), 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -68,6 +68,6 @@ hipError_t pg_launch_attn_mfma(const pg_layout& L, const void* q, const void* k,
 
 // Constants the host work list and the MFMA kernel agree on.
 constexpr int PG_WAVE_QUERIES = 32;   // query tokens per wave in the MFMA kernel
-constexpr int PG_ITEM_WAVES = 4;      // waves per work item (workgroup)
+constexpr int PG_ITEM_WAVES = 8;      // waves per work item (workgroup): two ping-pong groups of 4
 constexpr int PG_KEY_TILE = 64;       // keys per LDS tile
 constexpr int PG_XCDS = 8;            // XCDs of an MI355X; workgroup p runs on XCD p % 8

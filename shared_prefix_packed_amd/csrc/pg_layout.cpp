@@ -137,8 +137,8 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
 
     // --------------------------------------------------------- work list --
     // One item = query tokens [t0, t1) of one group x `hpw` query heads of one
-    // KV head. hpw = gcd(r, 4) heads share each LDS K/V tile (GQA reuse); the
-    // four waves of an item cover hpw heads x (4 / hpw) blocks of 32 tokens.
+    // KV head. hpw = gcd(r, 8) heads share each LDS K/V tile (GQA reuse); the
+    // eight waves of an item cover hpw heads x (8 / hpw) blocks of 32 tokens.
     const int r = num_q_heads / num_kv_heads;
     const int hpw = gcd_int(r, PG_ITEM_WAVES);
     const int BT = PG_WAVE_QUERIES * PG_ITEM_WAVES / hpw;

@@ -91,8 +91,8 @@ def _check_work_invariants(L, P, S, hq, hkv):
     items, spans = L.work()
     s = L.summary()
     hpw = s.heads_per_item
-    assert hpw == np.gcd(r, 4)
-    assert s.block_tokens == 128 // hpw
+    assert hpw == np.gcd(r, 8)
+    assert s.block_tokens == 256 // hpw
     cover = np.zeros((T, hq), dtype=np.int64)
     total_cost = 0
     xcd_of_cluster = {}
