@@ -122,8 +122,11 @@ pg_status pg_build_layout_host(int32_t num_groups, const int32_t* prefix_lens,
 /*
  * pg_layout_upload -- copy the device part of a layout (per-token descriptors,
  * work list, key spans, rotary frequencies) to the current HIP device, enqueued
- * on `stream`. Allocates one device buffer owned by the layout. Calling it
- * again is a no-op. PG_ERR_HIP / PG_ERR_OOM on failure.
+ * on `stream`. The image is written into pinned host memory and copied
+ * asynchronously into a device buffer owned by the layout; both come from a
+ * per-device cache of upload buffers that the library keeps until the process
+ * ends. Never waits for the device. Calling it again is a no-op.
+ * PG_ERR_HIP / PG_ERR_OOM on failure.
  */
 pg_status pg_layout_upload(pg_layout* layout, hipStream_t stream);
 
@@ -156,8 +159,12 @@ pg_status pg_layout_copy_tokens(const pg_layout* layout, int32_t* g0, int32_t* p
  * spans ([num_spans]); either may be NULL. */
 pg_status pg_layout_copy_work(const pg_layout* layout, pg_work_item* items, pg_key_span* spans);
 
-/* Free the layout and its device buffer. hipFree waits for the device, so
- * no enqueued call that uses the layout is cut short. NULL is ignored. */
+/* Free the layout. Returns at once: its upload buffer goes back to the cache
+ * and is reused only after the work already enqueued with this layout has
+ * completed on every stream it was used on (an event is recorded after each
+ * enqueue), so no pending call is cut short. A layout used on more than four
+ * distinct streams makes this call wait for its device instead. NULL is
+ * ignored. */
 void pg_layout_destroy(pg_layout* layout);
 
 /*

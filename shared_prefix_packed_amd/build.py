@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libpg.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["pg_layout.cpp", "pg_capi.cpp"]
+HOST_SOURCES = ["pg_layout.cpp", "pg_capi.cpp", "pg_pool.cpp"]
 HIP_SOURCES = ["pg_kernels.hip", "pg_attn_mfma.hip"]
 
 HIP_FLAGS = [

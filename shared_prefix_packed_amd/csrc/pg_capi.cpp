@@ -101,12 +101,12 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   const size_t off_sp = align_up(off_it + sizeof(pg_work_item) * L->items.size(), A);
   const size_t off_fr = align_up(off_sp + sizeof(pg_key_span) * L->spans.size(), A);
   const size_t bytes = align_up(off_fr + sizeof(double) * L->inv_freq.size(), A);
-  try {
-    L->staging.assign(bytes, 0);
-  } catch (const std::bad_alloc&) {
-    return pg_fail(PG_ERR_OOM, "host staging allocation failed");
-  }
-  unsigned char* h = L->staging.data();
+  hipError_t e = hipGetDevice(&L->device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  pg_slot* slot = nullptr;
+  pg_status st = pg_slot_acquire(L->device, bytes, &slot);
+  if (st != PG_OK) return st;
+  unsigned char* h = slot->host;
   std::memcpy(h + off_g0, L->tok_g0.data(), 4 * T);
   std::memcpy(h + off_pe, L->tok_pe.data(), 4 * T);
   std::memcpy(h + off_ss, L->tok_ss.data(), 4 * T);
@@ -115,21 +115,14 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   if (!L->spans.empty())
     std::memcpy(h + off_sp, L->spans.data(), sizeof(pg_key_span) * L->spans.size());
   std::memcpy(h + off_fr, L->inv_freq.data(), sizeof(double) * L->inv_freq.size());
-
-  hipError_t e = hipGetDevice(&L->device);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  void* d = nullptr;
-  e = hipMalloc(&d, bytes);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return e == hipErrorOutOfMemory ? pg_fail(PG_ERR_OOM, "hipMalloc(%zu) failed", bytes)
-                                    : hip_fail(e, "hipMalloc");
-  }
+  void* d = slot->dev;
   e = hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) {
-    (void)hipFree(d);
+    pg_slot_release(slot);
     return hip_fail(e, "hipMemcpyAsync");
   }
+  pg_slot_note_use(slot, stream);
+  L->slot = slot;
   unsigned char* b = static_cast<unsigned char*>(d);
   L->dev_buf = d;
   L->d_g0 = reinterpret_cast<const int32_t*>(b + off_g0);
@@ -202,7 +195,7 @@ pg_status pg_layout_copy_work(const pg_layout* L, pg_work_item* items, pg_key_sp
 
 void pg_layout_destroy(pg_layout* L) {
   if (!L) return;
-  if (L->dev_buf) (void)hipFree(L->dev_buf);
+  pg_slot_release(L->slot);   // reused only after the enqueued work that reads it
   delete L;
 }
 
@@ -212,6 +205,7 @@ pg_status pg_position_ids(const pg_layout* L, int64_t* pos, hipStream_t stream) 
   if (L->T == 0) return PG_OK;
   if (!pos) return pg_fail(PG_ERR_INVALID_ARG, "pos is NULL");
   hipError_t e = pg_launch_positions(*L, pos, stream);
+  pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "position-id kernel launch");
 }
 
@@ -225,6 +219,7 @@ pg_status pg_rope(const pg_layout* L, const int64_t* pos, const void* q_in, cons
   if (!pos || !q_in || !k_in || !q_out || !k_out)
     return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
   hipError_t e = pg_launch_rope(*L, pos, q_in, k_in, q_out, k_out, dtype, stream);
+  pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "rope kernel launch");
 }
 
@@ -243,6 +238,7 @@ pg_status pg_attn_fwd(const pg_layout* L, const void* q, const void* k, const vo
     e = pg_launch_attn_mfma(*L, q, k, v, o, lse, softmax_scale, stream);
   else
     e = pg_launch_attn_rowwise(*L, q, k, v, o, lse, dtype, softmax_scale, stream);
+  pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "attention kernel launch");
 }
 

@@ -3,10 +3,34 @@
 #pragma once
 
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "pg.h"
+
+// Upload buffer of a layout (pg_pool.cpp): pinned host staging plus a device
+// buffer, with one completion event per stream the layout was used on.
+constexpr int kSlotEvents = 4;
+struct pg_slot {
+  int device = -1;
+  size_t cap = 0;
+  unsigned char* host = nullptr;
+  void* dev = nullptr;
+  std::mutex mu;                       // guards the event list
+  hipEvent_t ev[kSlotEvents] = {};
+  hipStream_t stream[kSlotEvents] = {};
+  int nev = 0;
+  bool overflow = false;               // used on more streams than events
+  bool in_use = false;
+};
+// Takes an idle slot of at least `bytes` on `device` (the current device) or
+// makes one. Never waits for the device.
+pg_status pg_slot_acquire(int device, size_t bytes, pg_slot** out);
+// Records the slot's event for `stream` after work was enqueued there.
+void pg_slot_note_use(pg_slot* s, hipStream_t stream);
+// Returns the slot; it is reused once its recorded events have completed.
+void pg_slot_release(pg_slot* s);
 
 struct pg_layout {
   // shape
@@ -32,10 +56,10 @@ struct pg_layout {
   int64_t max_item_cost = 0;
   std::vector<int64_t> xcd_load;   // summed item cost per XCD queue
 
-  // device copy (one allocation, filled by pg_layout_upload)
+  // device copy (one upload slot, filled by pg_layout_upload)
   int device = -1;
   void* dev_buf = nullptr;
-  std::vector<unsigned char> staging;   // host image of dev_buf, kept alive for the async copy
+  pg_slot* slot = nullptr;
   const int32_t* d_g0 = nullptr;
   const int32_t* d_pe = nullptr;
   const int32_t* d_ss = nullptr;

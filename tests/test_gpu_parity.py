@@ -343,3 +343,33 @@ def test_packed_equals_unpacked_on_gpu():
     d_l = (lu - lse[:, idx]).abs().max().item()
     say(f"  unpacked vs packed: max|dO|={d_o:.3e} max|dlse|={d_l:.3e}")
     assert d_o <= 2 * O_TOL and d_l <= 2 * LSE_TOL
+
+
+def test_layouts_destroyed_while_work_is_in_flight():
+    """pg_layout_destroy returns at once and recycles the upload buffer only
+    after the enqueued work that reads it has finished: layouts of different
+    sizes built and destroyed behind a long-running kernel all give the
+    oracle's results."""
+    shapes = [([5, 9], [[3, 4], [2, 6, 1]]), ([300], [[1, 40, 0, 200, 33]]),
+              ([31, 33, 64], [[32, 1], [63, 65], [128, 129, 127]]), ([0, 7], [[4, 3], [5]])]
+    a = torch.randn(4096, 4096, device="cuda")
+    say("layout recycling: 12 layouts destroyed behind a busy stream")
+    outs = []
+    for rep in range(3):
+        b = a @ a          # keeps the stream busy while the layouts below are recycled
+        for P, S in shapes:
+            w = make_custom(P, S, num_q_heads=4, num_kv_heads=1)
+            L = layout_of(w)
+            pos = pg.pg_position_ids(L)
+            qkv = draw_qkv(w)
+            q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
+            o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+            L.close()
+            outs.append((w, qkv, pos, o, lse))
+    torch.cuda.synchronize()
+    del b
+    for w, qkv, pos, o, lse in outs:
+        lay = oracle_layout(w)
+        assert np.array_equal(pos.cpu().numpy(), O.positions(lay))
+        check_attn(w, o, lse, host_vals(w, qkv["q"]), host_vals(w, qkv["k"]),
+                   host_vals(w, qkv["v"]), lay, full=True)
