@@ -37,7 +37,13 @@
 // 16-key step, 8-key half and 32-d block one 512-byte block, in which lane s of
 // every 16-lane group owns 8 bytes; one such read then hands each lane 4 keys
 // of one d, which is exactly an MFMA A-operand fragment of V^T. The key order
-// inside each 16-key step is the one the S^T accumulators give P.
+// inside each 16-key step is the one the S^T accumulators give P. A wave
+// issues the operand reads of its first four PV products at the end of its
+// VALU step, so the MFMA step starts without waiting on LDS.
+//
+// Output. The normalised O^T tile of each wave goes through LDS once the ring
+// is idle, so that O leaves in whole 256-byte rows (16 bytes per lane) rather
+// than as 32 scattered 16-byte pieces per store.
 #include <hip/hip_runtime.h>
 
 #include "pg_internal.h"
@@ -132,17 +138,27 @@ constexpr float RESCALE_SLACK = 8.0f;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Value of lane l ^ 32 (the other half of the wave), through a VALU lane swap
+// instead of an LDS round trip.
+__device__ inline float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // r[0] holds lanes 0-31 in both halves, r[1] lanes 32-63 in both halves
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // s_waitcnt vmcnt(N) (gfx9 encoding: expcnt and lgkmcnt fields left at "no wait").
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ inline void wait_vmem_but_one_tile() { __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE); }
 
-// End of a ping-pong step: this wave's LDS accesses done, then the workgroup
-// barrier. Global loads stay in flight across it (a __syncthreads() fence would
-// drain them). The asm's memory clobber keeps the compiler from moving memory
+// End of a ping-pong step: the workgroup barrier alone. Tile fetches and LDS
+// reads may stay in flight across it (a __syncthreads() fence would drain
+// both): every LDS read is consumed by the step after the one that issued it
+// at the latest, and a ring stage is refilled two barriers after its last
+// read. The asm's memory clobber keeps the compiler from moving memory
 // operations across; the scheduling barriers keep arithmetic on its side.
 __device__ inline void step_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -320,6 +336,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   bool p_part = false;   // this wave holds P of the tile awaiting PV
   int v_ka = 0, v_k1 = 0;
   bool v_prefix = true, v_full = true;
+  i16x4_t vpre[8];   // first PV operand reads, issued at the end of the VALU step
 
   // One MFMA step (n) and one VALU step (softmax of tile n), as lambdas; group
   // A runs [M(n); V(n)] and group B [V(n-1); M(n)], so that across a loop back
@@ -333,8 +350,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const i16x4_t lo = lds_read_tr(vb + 512 * (8 * ks + db));
-          const i16x4_t hi = lds_read_tr(vb + 512 * (8 * ks + 4 + db));
+          const int j = 4 * ks + db;
+          const i16x4_t lo = j < 4 ? vpre[2 * j] : lds_read_tr(vb + 512 * (8 * ks + db));
+          const i16x4_t hi = j < 4 ? vpre[2 * j + 1] : lds_read_tr(vb + 512 * (8 * ks + 4 + db));
           const bf16x8_t av = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks], acc[db], 0, 0, 0);
@@ -342,7 +360,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       }
       // issue order: 6 reads ahead, then (1 MFMA, 2 reads), so LDS latency
       // hides behind the matrix core instead of stalling it
-      sched_reads_ahead<6, 2, 16>();
+      sched_reads_ahead<0, 2, 12>();
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     // keep PV(n-1) ahead of S(n): P dies before the S accumulators are born
     __builtin_amdgcn_sched_barrier(0);
@@ -401,20 +420,35 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
         const int base = v_ka + 4 * half;
         const int lo = (v_prefix ? v_ka : ss_t) - base;
         const int hi = min(tq, v_k1 - 1) - base;
+        if (__ballot(lo > 0) == 0ull) {
+          // no lane has a lower bound inside the tile (diagonal and span-end
+          // tiles): one compare per score
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+          for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-            sacc[kb2][i] = (c >= lo && c <= hi) ? sacc[kb2][i] : -__builtin_inff();
-          }
+            for (int i = 0; i < 16; ++i) {
+              const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+              sacc[kb2][i] = (c <= hi) ? sacc[kb2][i] : -__builtin_inff();
+            }
+        } else {
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+              sacc[kb2][i] = (c >= lo && c <= hi) ? sacc[kb2][i] : -__builtin_inff();
+            }
+        }
       }
       float mt = sacc[0][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sacc[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[1][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
       const float mt2 = mt * a.c_log2;
       // rescale (wave-uniform decision) only when some row's max grew a lot
       if (__ballot(mt2 > m_run + RESCALE_SLACK) != 0ull) {
@@ -445,6 +479,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
         pf[ks] = as_bf16x8(pk);
       }
       l_run += lsum;
+      // first operand reads of PV(n), used by the next MFMA step: tile n's V
+      // was published before an earlier barrier
+      const unsigned char* vb = smem + (n % NSTAGE) * STAGE + voff;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vpre[2 * j] = lds_read_tr(vb + 512 * j);
+        vpre[2 * j + 1] = lds_read_tr(vb + 512 * (4 + j));
+      }
     }
     s_part = false;
     // Tile n+1 (fetched by this group in M(n-1)) must have landed before the
@@ -472,23 +514,41 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
     }
   }
 
+  // no tile fetch may still be landing in the ring, and no wave still reads it
+  wait_vmem_all();
+  __syncthreads();
+
   // ---- epilogue -----------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (row_valid) {
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = a.o + (int64_t(tq) * a.Hq + h) * D;
-    // O^T C-layout: register i of block db holds d = 32 db + 8 (i/4) + 4 half + i%4.
+  // O^T C-layout: register i of block db holds d = 32 db + 8 (i/4) + 4 half +
+  // i%4 of query column qi. The tile goes through this wave's 8 KB of the
+  // (now idle) ring, 16-byte chunks XOR-swizzled by row, so that each store
+  // below writes whole 256-byte rows of O.
+  const float l_tot = l_run + other_half(l_run);
+  const float inv = 1.f / l_tot;
+  unsigned char* ot = smem + 8192 * wave;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * half;
-        const uint2 w = make_uint2(pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
-                                   pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv));
-        *reinterpret_cast<uint2*>(orow + d0) = w;
-      }
-    if (a.lse && half == 0)
-      a.lse[int64_t(h) * a.T + tq] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * half;   // 4 values, 8 bytes
+      const uint2 w = make_uint2(pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
+                                 pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv));
+      const int chunk = (d0 >> 3) ^ (qi & 15);
+      *reinterpret_cast<uint2*>(ot + qi * 256 + 16 * chunk + 8 * half) = w;
+    }
+  if (wave_active && a.lse && half == 0 && row_valid)
+    a.lse[int64_t(h) * a.T + tq] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's tile is in LDS
+  if (wave_active) {
+    // lane: row 4 it + lane / 16, chunk lane % 16
+#pragma unroll
+    for (int it2 = 0; it2 < 8; ++it2) {
+      const int r = 4 * it2 + (lane >> 4);
+      const int c = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(ot + r * 256 + 16 * (c ^ (r & 15)));
+      if (tb + r < te)
+        *reinterpret_cast<uint4*>(a.o + (int64_t(tb + r) * a.Hq + h) * D + 8 * c) = v;
+    }
   }
 }
 
