@@ -29,6 +29,9 @@ Readings where the pages are silent (each listed in the design doc):
   * lse is the natural log of the sum of exp of the *scaled* scores.
   * zero-length suffixes occupy no tokens; P = 0 and n = 0 are legal.
 
+The backward (``attention_backward``) is the chain rule of that definition
+written out for an upstream gradient of O; tests/test_oracle_backward.py pins it.
+
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (hand-derived values, closed forms, a library routine, brute
 force); the pins are listed beside each function.
@@ -402,6 +405,86 @@ def attention_rows(q, k, v, lay, scale: float, num_q_heads: int,
         out_o[n] = (p @ vv) / p.sum()
         out_l[n] = m + math.log(p.sum())
     return out_o, out_l
+
+
+# ------------------------------------------------------------------ backward --
+
+
+def group_mask(lay, g: int) -> np.ndarray:
+    """Allowed (query, key) pairs inside group g as an n_g x n_g boolean matrix
+    (row = query, column = key, both indexed from the group's first token):
+    key j is allowed for query i iff j <= i and (j is a prompt token or i and
+    j lie in the same response). Same reading as ``allowed_keys``."""
+    a, b = int(lay["group_off"][g]), int(lay["group_off"][g + 1])
+    pe = int(lay["pe"][a]) if b > a else a
+    ss = np.asarray(lay["ss"][a:b], dtype=np.int64)
+    t = np.arange(a, b)
+    i = t[:, None]
+    j = t[None, :]
+    return (j <= i) & ((j < pe) | (ss[:, None] == ss[None, :]))
+
+
+def attention_backward(q, k, v, do, lay, scale: float, num_q_heads: int,
+                       num_kv_heads: int, groups: Sequence[int] = None):
+    """Gradients of the packed attention output, by the chain rule.
+
+    The packed forward (``attention``) maps Q, K, V to O with one softmax per
+    (token, head) over its key set. Its derivative, for an upstream gradient dO
+    of O (the lse output is treated as carrying no gradient), is written out
+    per group and query head in fp64:
+      P  = softmax(scale * Q K^T) over the allowed keys (rows = queries),
+      dV = P^T dO,           dP = dO V^T,
+      D  = rowsum(P * dP) = rowsum(dO * O),
+      dS = P * (dP - D),     dQ = scale * dS K,   dK = scale * dS^T Q.
+    Under GQA a KV head's dK and dV sum the contributions of all its query
+    heads. A prompt key therefore collects gradient from every response of its
+    group, since the prompt is stored once (Preference Packing, core idea).
+
+    q, do: [T, Hq, d]; k, v: [T, Hkv, d]. Returns (dq [T, Hq, d], dk, dv
+    [T, Hkv, d]) in fp64, computed for ``groups`` (default: all) and zero
+    elsewhere. Dense per group: for groups of up to a few thousand tokens.
+    Pinned by: central finite differences of sum(dO * O) with ``attention``;
+    torch's float64 SDPA autograd on the unpacked sequences (library routine);
+    closed forms (constant V gives dQ = dK = 0; the keys' dV sum to the
+    queries' dO sum; a group's first token has dQ = 0).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    T, Hq, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    if groups is None:
+        groups = range(len(lay["prefix_lens"]))
+    for g in groups:
+        a, b = int(lay["group_off"][g]), int(lay["group_off"][g + 1])
+        if b == a:
+            continue
+        M = group_mask(lay, g)
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, num_kv_heads)
+            Q, K, V, dO = q[a:b, h], k[a:b, hk], v[a:b, hk], do[a:b, h]
+            s = np.where(M, scale * (Q @ K.T), -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            P = e / e.sum(axis=1, keepdims=True)
+            O = P @ V
+            dP = dO @ V.T
+            D = (dO * O).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[a:b, h] = scale * (dS @ K)
+            dk[a:b, hk] += scale * (dS.T @ Q)
+            dv[a:b, hk] += P.T @ dO
+    return dq, dk, dv
+
+
+def backward_flop(lay, head_dim: int, num_q_heads: int) -> int:
+    """Algorithmic FLOP of the backward: five products over the allowed pairs
+    (S = QK^T recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q),
+    2 d FLOP each per pair and query head: 10 d Hq per allowed pair."""
+    return 10 * head_dim * num_q_heads * useful_pairs(lay)
 
 
 # ---------------------------------------------------------- FLOP accounting --

@@ -1,0 +1,158 @@
+"""Pins of the oracle's backward (``attention_backward``) against things other
+than itself: finite differences of the forward, torch's float64 SDPA autograd
+on the unpacked sequences, and closed forms. CPU only."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pg_oracle as O
+from workloads import draw_qkv, make_custom, make_workload
+
+CASES = [
+    ([3, 0], [[2, 1], [2]], 2, 1, 4),      # prompt-less group, two responses
+    ([4], [[3, 0, 2]], 4, 2, 8),           # empty response in the middle, GQA 2
+    ([1, 2], [[1, 1, 1], []], 3, 3, 4),    # one-token prompt, response-less group
+]
+
+
+def _inputs(P, S, hq, hkv, d, seed=0):
+    w = make_custom(P, S, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype="f32", seed=seed)
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    x = draw_qkv(w)
+    r = np.random.default_rng(100 + seed)
+    do = r.standard_normal(x["q"].shape)
+    return w, lay, x["q"].astype(np.float64), x["k"].astype(np.float64), x["v"].astype(np.float64), do
+
+
+def _loss(q, k, v, do, lay, w):
+    o, _ = O.attention(q, k, v, lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_backward_matches_finite_differences(case):
+    w, lay, q, k, v, do = _inputs(*case)
+    dq, dk, dv = O.attention_backward(q, k, v, do, lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            xp = x.copy(); xp[i] += eps
+            xm = x.copy(); xm[i] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, lay, w)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, lay, w)
+            num[i] = (lp - lm) / (2 * eps)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(g).max()), name
+
+
+def _torch_unpacked_grads(w, lay, q, k, v, do):
+    """Gradients by torch's float64 SDPA autograd over the unpacked sequences.
+    Prompt tensors are shared leaves (so their K/V gradients sum over the
+    responses); the prompt rows' output gradient is routed to the first
+    sequence of the group only, because the packed batch holds those rows
+    once."""
+    Hq, Hkv = w.num_q_heads, w.num_kv_heads
+    r = Hq // Hkv
+    T, _, d = q.shape
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    tdo = torch.tensor(do)
+    loss = 0.0
+    seen = set()
+    for g, p0, P, (s0, s1) in O.sequences(lay):
+        idx = torch.tensor(list(range(p0, p0 + P)) + list(range(s0, s1)), dtype=torch.long)
+        if len(idx) == 0:
+            continue
+        qs = tq[idx].transpose(0, 1)                              # [Hq, L, d]
+        ks = tk[idx].transpose(0, 1).repeat_interleave(r, dim=0)  # [Hq, L, d]
+        vs = tv[idx].transpose(0, 1).repeat_interleave(r, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qs.unsqueeze(0), ks.unsqueeze(0), vs.unsqueeze(0), is_causal=True,
+            scale=w.softmax_scale)[0].transpose(0, 1)             # [L, Hq, d]
+        weight = torch.ones(len(idx), 1, 1, dtype=torch.float64)
+        if g in seen:
+            weight[:P] = 0.0
+        seen.add(g)
+        loss = loss + (o * tdo[idx] * weight).sum()
+    loss.backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_backward_matches_torch_on_unpacked_sequences(case):
+    w, lay, q, k, v, do = _inputs(*case, seed=3)
+    dq, dk, dv = O.attention_backward(q, k, v, do, lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    rq, rk, rv = _torch_unpacked_grads(w, lay, q, k, v, do)
+    assert np.abs(dq - rq).max() < 1e-10
+    assert np.abs(dk - rk).max() < 1e-10
+    assert np.abs(dv - rv).max() < 1e-10
+
+
+def test_backward_matches_torch_on_tiny_workload():
+    w = make_workload(0)
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    x = draw_qkv(w)
+    q, k, v = (x[n].astype(np.float64) for n in ("q", "k", "v"))
+    do = np.random.default_rng(7).standard_normal(q.shape)
+    dq, dk, dv = O.attention_backward(q, k, v, do, lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    rq, rk, rv = _torch_unpacked_grads(w, lay, q, k, v, do)
+    for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.abs(a - b).max() < 1e-10
+
+
+def test_backward_closed_forms():
+    w, lay, q, k, v, do = _inputs([5, 2], [[3, 4], [1, 2]], 4, 2, 8, seed=5)
+    dq, dk, dv = O.attention_backward(q, k, v, do, lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    r = w.num_q_heads // w.num_kv_heads
+    # rows of P sum to one: summed over keys, dV equals dO summed over queries
+    for hk in range(w.num_kv_heads):
+        assert np.allclose(dv[:, hk].sum(axis=0), do[:, hk * r:(hk + 1) * r].sum(axis=(0, 1)), atol=1e-12)
+    # a group's first token sees only itself: P = 1, dS = 0
+    for g in range(2):
+        assert np.abs(dq[int(lay["group_off"][g])]).max() < 1e-12
+    # the same V for every key: O does not depend on the scores at all
+    vc = np.broadcast_to(v[:1], v.shape).copy()
+    dq2, dk2, _ = O.attention_backward(q, k, vc, do, lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    assert np.abs(dq2).max() < 1e-12 and np.abs(dk2).max() < 1e-12
+
+
+def test_finite_differences_catch_a_dropped_term():
+    """A plausible mistake (dS = P dP, the D term dropped) fails the pin."""
+    w, lay, q, k, v, do = _inputs(*CASES[0])
+    dq, _, _ = O.attention_backward(q, k, v, do, lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    # the mistaken gradient, rebuilt from the same pieces without the D term
+    bad = np.zeros_like(dq)
+    for g in range(len(lay["prefix_lens"])):
+        a, b = int(lay["group_off"][g]), int(lay["group_off"][g + 1])
+        if b == a:
+            continue
+        M = O.group_mask(lay, g)
+        for h in range(w.num_q_heads):
+            hk = h // (w.num_q_heads // w.num_kv_heads)
+            s = np.where(M, w.softmax_scale * (q[a:b, h] @ k[a:b, hk].T), -np.inf)
+            P = np.exp(s - s.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            bad[a:b, h] = w.softmax_scale * ((P * (do[a:b, h] @ v[a:b, hk].T)) @ k[a:b, hk])
+    eps = 1e-6
+    num = np.zeros_like(q)
+    it = np.nditer(q, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp = q.copy(); xp[i] += eps
+        xm = q.copy(); xm[i] -= eps
+        num[i] = (_loss(xp, k, v, do, lay, w) - _loss(xm, k, v, do, lay, w)) / (2 * eps)
+    assert np.abs(num - dq).max() < 1e-6
+    assert np.abs(num - bad).max() > 1e-3
+
+
+def test_backward_flop_count():
+    w = make_workload(0)
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    # 217 allowed pairs (hand-derived), d = 64, one query head
+    assert O.backward_flop(lay, 64, 1) == 10 * 64 * 217

@@ -156,6 +156,8 @@ def make_custom(prefix_lens: Sequence[int], suffix_lens: Sequence[Sequence[int]]
                 softmax_scale: Optional[float] = None, seed: int = 0,
                 name: str = "custom") -> Workload:
     """A workload with explicit lengths (edge cases: P = 0, n = 0, S = 0)."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', not {dtype!r}")
     if len(prefix_lens) != len(suffix_lens):
         raise ValueError("one suffix list per group")
     flat = [int(x) for grp in suffix_lens for x in grp]
