@@ -69,6 +69,8 @@ typedef struct pg_layout_summary {
                               prefix+suffix sequence (the work packing avoids)   */
   int64_t max_item_cost;   /* largest work item, in (query, key) pairs x heads   */
   int64_t max_xcd_cost;    /* largest per-XCD sum of item costs (balance check)  */
+  int32_t num_kv_items;    /* work items of the backward dK/dV launch            */
+  int32_t reserved;        /* 0                                                  */
 } pg_layout_summary;
 
 /* One work item of the attention launch: query tokens [t0, t1) of one group,
@@ -86,6 +88,20 @@ typedef struct pg_work_item {
   int32_t nspan;
   int64_t cost;   /* allowed (query, key) pairs of the item x its heads      */
 } pg_work_item;
+
+/* One work item of the backward dK/dV launch: keys [k0, k1) of KV head hk,
+ * inside one segment (prompt or one response) of one group, at most 128 keys.
+ * Every query that reads these keys lies in [k0, qend): qend is the group's end
+ * for prompt keys and the response's end for response keys. Stored in launch
+ * order like pg_work_item (XCD p % 8, clusters of one group and KV head on one
+ * XCD); items with k0 == k1 are padding. */
+typedef struct pg_kv_item {
+  int32_t k0;
+  int32_t k1;
+  int32_t hk;
+  int32_t qend;
+  int64_t cost;   /* (query, key) pairs of the item x the r query heads      */
+} pg_kv_item;
 
 /* A contiguous key range [k0, k1) inside one segment of one group. */
 typedef struct pg_key_span {
@@ -159,6 +175,9 @@ pg_status pg_layout_copy_tokens(const pg_layout* layout, int32_t* g0, int32_t* p
  * spans ([num_spans]); either may be NULL. */
 pg_status pg_layout_copy_work(const pg_layout* layout, pg_work_item* items, pg_key_span* spans);
 
+/* Host copy of the backward dK/dV work list: items [num_kv_items]. */
+pg_status pg_layout_copy_kv_work(const pg_layout* layout, pg_kv_item* items);
+
 /* Free the layout. Returns at once: its upload buffer goes back to the cache
  * and is reused only after the work already enqueued with this layout has
  * completed on every stream it was used on (an event is recorded after each
@@ -214,6 +233,29 @@ pg_status pg_rope(const pg_layout* layout, const int64_t* pos, const void* q_in,
  */
 pg_status pg_attn_fwd(const pg_layout* layout, const void* q, const void* k, const void* v,
                       void* o, float* lse, pg_dtype dtype, float softmax_scale,
+                      hipStream_t stream);
+
+/*
+ * pg_attn_bwd -- gradients of pg_attn_fwd's output O for an upstream gradient
+ * dO: dQ, dK, dV. The derivative of the packed attention, by the chain rule:
+ * with P the softmax of a row over its key set, dV = P^T dO, dS = P (dO V^T -
+ * D) with D = rowsum(dO * O), dQ = scale dS K, dK = scale dS^T Q; KV heads sum
+ * over their query heads. A prompt key is stored once, so its dK and dV collect
+ * the gradient of every response of its group ("Preference Packing", core
+ * idea: the prompt's attention is shared by all responses). lse carries no
+ * gradient. Recomputes P from Q, K and the forward's lse.
+ *  q, k, v     the forward's inputs (after RoPE)
+ *  o, lse      the forward's outputs for the same inputs (lse fp32 [Hq, T])
+ *  dout        dO [T, Hq, d]
+ *  dq          [T, Hq, d], dk, dv [T, Hkv, d]: written completely (every row of
+ *              dk/dv is written, zero where no query reads the key)
+ *  delta       caller-owned device scratch of Hq * T floats (D per row)
+ * All tensors share dtype; PG_ERR_UNSUPPORTED unless dtype == PG_BF16 and
+ * d == 128. dq, dk, dv must not alias the inputs or each other.
+ */
+pg_status pg_attn_bwd(const pg_layout* layout, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                      void* dv, float* delta, pg_dtype dtype, float softmax_scale,
                       hipStream_t stream);
 
 /* Static text for a status code. */

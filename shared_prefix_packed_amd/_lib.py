@@ -35,6 +35,8 @@ class LayoutSummary(ctypes.Structure):
         ("unpacked_pairs", c_int64),
         ("max_item_cost", c_int64),
         ("max_xcd_cost", c_int64),
+        ("num_kv_items", c_int32),
+        ("reserved", c_int32),
     ]
 
 
@@ -45,6 +47,11 @@ class WorkItem(ctypes.Structure):
 
 class KeySpan(ctypes.Structure):
     _fields_ = [("k0", c_int32), ("k1", c_int32)]
+
+
+class KvItem(ctypes.Structure):
+    _fields_ = [("k0", c_int32), ("k1", c_int32), ("hk", c_int32), ("qend", c_int32),
+                ("cost", c_int64)]
 
 
 # name -> (restype, argtypes); every symbol include/pg.h declares
@@ -59,12 +66,16 @@ SIGNATURES = {
     "pg_layout_copy_tokens": (c_int32, [c_void_p, P_int32, P_int32, P_int32]),
     "pg_layout_copy_work": (c_int32, [c_void_p, ctypes.POINTER(WorkItem),
                                       ctypes.POINTER(KeySpan)]),
+    "pg_layout_copy_kv_work": (c_int32, [c_void_p, ctypes.POINTER(KvItem)]),
     "pg_layout_destroy": (None, [c_void_p]),
     "pg_position_ids": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "pg_rope": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                           c_void_p]),
     "pg_attn_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_int32, ctypes.c_float, c_void_p]),
+    "pg_attn_bwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                              ctypes.c_float, c_void_p]),
     "pg_status_string": (ctypes.c_char_p, [c_int32]),
     "pg_last_error": (ctypes.c_char_p, []),
 }

@@ -12,7 +12,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import KeySpan, LayoutSummary, WorkItem, check, load
+from ._lib import KeySpan, KvItem, LayoutSummary, WorkItem, check, load
 
 
 def _i32(x) -> np.ndarray:
@@ -92,6 +92,15 @@ class Layout:
                                                   ("nspan", "<i4"), ("cost", "<i8")]))
         sp = np.frombuffer(spans, dtype=np.int32).reshape(-1, 2)
         return it[:s.num_items].copy(), sp[:s.num_spans].copy()
+
+    def kv_work(self) -> np.ndarray:
+        """Backward dK/dV work items (structured array, launch order)."""
+        s = self.summary()
+        items = (KvItem * max(1, s.num_kv_items))()
+        check(load().pg_layout_copy_kv_work(self.handle, items), "pg_layout_copy_kv_work")
+        it = np.frombuffer(items, dtype=np.dtype([("k0", "<i4"), ("k1", "<i4"), ("hk", "<i4"),
+                                                  ("qend", "<i4"), ("cost", "<i8")]))
+        return it[:s.num_kv_items].copy()
 
 
 def _layout_args(prefix_lens, suffix_counts, suffix_lens):
@@ -207,3 +216,35 @@ def pg_attn_fwd(layout: Layout, q, k, v, softmax_scale: float, o=None, lse=None,
                              _dtype_code(q), float(softmax_scale), _stream_handle(stream)),
           "pg_attn_fwd")
     return o, lse
+
+
+def pg_attn_bwd(layout: Layout, q, k, v, o, lse, dout, softmax_scale: float, dq=None, dk=None,
+                dv=None, delta=None, stream=None):
+    """Packed attention backward for an upstream gradient dout of the forward's
+    o (lse: the forward's fp32 [Hq, T]). Returns (dq, dk, dv)."""
+    import torch
+    T, Hq, Hkv, d = layout.total_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    _check_tensor("q", q, (T, Hq, d))
+    _check_tensor("k", k, (T, Hkv, d), q.dtype)
+    _check_tensor("v", v, (T, Hkv, d), q.dtype)
+    _check_tensor("o", o, (T, Hq, d), q.dtype)
+    _check_tensor("dout", dout, (T, Hq, d), q.dtype)
+    _check_tensor("lse", lse, (Hq, T), torch.float32)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    if delta is None:
+        delta = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _check_tensor("dq", dq, (T, Hq, d), q.dtype)
+    _check_tensor("dk", dk, (T, Hkv, d), q.dtype)
+    _check_tensor("dv", dv, (T, Hkv, d), q.dtype)
+    _check_tensor("delta", delta, (Hq, T), torch.float32)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    check(load().pg_attn_bwd(layout.handle, ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(dout),
+                             ptr(dq), ptr(dk), ptr(dv), ptr(delta), _dtype_code(q),
+                             float(softmax_scale), _stream_handle(stream)),
+          "pg_attn_bwd")
+    return dq, dk, dv

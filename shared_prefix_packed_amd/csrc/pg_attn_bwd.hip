@@ -1,0 +1,632 @@
+// Packed shared-prefix attention backward, bf16, d = 128, for gfx950 (CDNA4).
+//
+// The derivative of the forward (pg_attn_fwd) for an upstream gradient dO, by
+// the chain rule: with P the softmax of a query row over its key set K(t),
+//   dV = P^T dO,  dS = P * (dO V^T - D),  D = rowsum(dO * O),
+//   dQ = scale * dS K,  dK = scale * dS^T Q,
+// summed over the query heads of each KV head. The prompt is stored once
+// ("Preference Packing", core idea), so a prompt key's dK and dV collect the
+// gradient of every response of its group. P is recomputed from Q, K and the
+// forward's lse, so no attention matrix is kept.
+//
+// Three launches:
+//  * bwd_delta_kernel: D for every (token, head) row.
+//  * bwd_dq_kernel: the forward's work items (query blocks x heads). Per wave
+//    32 query rows; per 64-key tile of the item's key spans
+//      S^T = K Q^T, dP^T = V dO^T           (A = K, V rows from LDS)
+//      P^T = exp2(S^T c - lse2), dS^T = P^T (dP^T - D)
+//      dQ^T += K^T dS^T                     (A = K^T by transposing LDS reads,
+//                                            B = dS^T from the accumulators)
+//    so Q, dO and dQ stay in registers and each key tile is staged once for
+//    the eight waves.
+//  * bwd_dkv_kernel: key blocks of at most 128 keys of one KV head inside one
+//    segment. The queries that read key j are one contiguous range [j, qend)
+//    (the group's end for a prompt key, the response's end otherwise), taken
+//    in tiles of 32 rows for each of the r query heads. Per wave 32 keys:
+//      S = Q K^T, dP = dO V^T                (A = Q, dO rows from LDS)
+//      P, dS as above (lse and D per query row from LDS)
+//      dV += P^T dO, dK += dS^T Q           (A = P^T, dS^T from the
+//                                            accumulators, B = dO, Q by
+//                                            transposing LDS reads)
+//    so K, V, dK and dV stay in registers for the whole block and no atomics
+//    are needed.
+// Tiles go HBM -> LDS with buffer loads that write LDS (as in the forward),
+// three stages deep, with one workgroup barrier per tile.
+#include <hip/hip_runtime.h>
+
+#include "pg_hip_common.h"
+#include "pg_internal.h"
+
+namespace {
+
+using namespace pg_hip;
+
+constexpr int D = 128;
+constexpr float LOG2E = 1.44269504088896340736f;
+
+// ------------------------------------------------------------------ helpers --
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 4 bytes per lane from buffer `r` at byte offset `voff` into LDS at
+// lds + 4 * lane (M0 written one wait state before the load, as for the
+// 16-byte form).
+__device__ inline void buf4_to_lds(i32x4_t r, int voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(lds)
+      : "memory");
+}
+
+// Byte offset (from a tile's first row) of the 16-byte global unit that lane
+// `lane` of 1 KB block `b` brings into a row-major tile: row 4 b + lane / 16,
+// stored chunk lane % 16 holding global chunk (lane % 16) ^ (row % 16).
+__device__ inline int rowmajor_off(int b, int lane, int row_bytes) {
+  const int row = 4 * b + (lane >> 4);
+  const int chunk = (lane & 15) ^ (row & 15);
+  return row * row_bytes + 16 * chunk;
+}
+
+// Byte offset of the 16-byte global unit that lane `lane` of 1 KB block `b`
+// brings into a tile laid out for transposing reads: 512-byte read block
+// rb = 2 b + lane / 32 (index 8 ks + 4 rd + db) holds, at 16-byte unit u,
+// row 16 ks + 8 rd + 4 (u/16) + (u%8)/2 and d = 32 db + 16 ((u/8)&1) + 8 (u&1).
+__device__ inline int trread_off(int b, int lane, int row_bytes) {
+  const int rb = 2 * b + (lane >> 5);
+  const int ks = rb >> 3, rd = (rb >> 2) & 1, db = rb & 3;
+  const int u = lane & 31, g = u >> 3;
+  const int row = 16 * ks + 8 * rd + 4 * (g >> 1) + ((u & 7) >> 1);
+  const int d0 = 32 * db + 16 * (g & 1) + 8 * (u & 1);
+  return row * row_bytes + 2 * d0;
+}
+
+// The two transposing reads that form one MFMA operand fragment (8 bf16: rows
+// 16 ks .. 16 ks + 15 of column 32 db + lane % 32 in the accumulators' order).
+__device__ inline bf16x8_t tr_operand(const unsigned char* vb, int ks, int db) {
+  const i16x4_t lo = lds_read_tr(vb + 512 * (8 * ks + db));
+  const i16x4_t hi = lds_read_tr(vb + 512 * (8 * ks + 4 + db));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Accumulator registers of a 32x32 block (row 8 (i/4) + 4 half + i%4) packed
+// as the operand of the 16-row step s (rows 16 s .. 16 s + 15): registers
+// 8 (s & 1) + 0..7 of block s / 2.
+__device__ inline bf16x8_t pack_step(const f32x16_t& c, int s) {
+  uint4 pk;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int i = 8 * (s & 1) + 2 * jj;
+    (&pk.x)[jj] = pack_bf16x2(c[i], c[i + 1]);
+  }
+  return as_bf16x8(pk);
+}
+
+// Writes a 32 x 128 fp32 tile held as four 32x32 accumulator blocks (block db
+// covers d = 32 db .. 32 db + 31), scaled by `mul` and rounded to bf16,
+// through LDS region `ot` (8 KB, 16-byte chunks XOR-swizzled by row) to the
+// global rows dst + row * row_elems, rows [0, nrows), as whole 256-byte rows.
+// ROWS_ARE_REGS: the accumulator rows (register i: row 8 (i/4) + 4 half + i%4)
+// are the tile rows and the lanes are d; otherwise the lanes are the tile rows
+// and the registers are d.
+template <bool ROWS_ARE_REGS>
+__device__ inline void store_tile(const f32x16_t* acc, float mul, unsigned char* ot, int lane,
+                                  uint16_t* dst, int64_t row_elems, int nrows) {
+  const int col = lane & 31, half = lane >> 5;
+  if constexpr (!ROWS_ARE_REGS) {
+    // lane = tile row (query), registers = d: 4 consecutive d per 8 bytes
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * half;
+        const uint2 w = make_uint2(pack_bf16x2(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                                   pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul));
+        const int chunk = (d0 >> 3) ^ (col & 15);
+        *reinterpret_cast<uint2*>(ot + col * 256 + 16 * chunk + 8 * half) = w;
+      }
+  } else {
+    // registers = tile row (key), lane = d: one bf16 per element
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+        const int d = 32 * db + col;
+        const int chunk = (d >> 3) ^ (row & 15);
+        const __bf16 b = static_cast<__bf16>(acc[db][i] * mul);   // nearest-even
+        *reinterpret_cast<__bf16*>(ot + row * 256 + 16 * chunk + 2 * (d & 7)) = b;
+      }
+  }
+  wait_lds();
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = 4 * it + (lane >> 4);
+    const int c = lane & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(ot + r * 256 + 16 * (c ^ (r & 15)));
+    if (r < nrows) *reinterpret_cast<uint4*>(dst + int64_t(r) * row_elems + 8 * c) = v;
+  }
+}
+
+// ------------------------------------------------------------------- delta --
+
+// D[h][t] = sum_d dO[t,h,d] O[t,h,d] in fp32; 16 lanes per (t, h) row.
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const uint16_t* dout,
+                                                        float* delta, int T, int Hq) {
+  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);   // t * Hq + h
+  const int sub = threadIdx.x & 15;
+  const int64_t rows = int64_t(T) * Hq;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 a = ldg16(o + row * D + 8 * sub);
+    const uint4 b = ldg16(dout + row * D + 8 * sub);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = (&a.x)[j], y = (&b.x)[j];
+      acc = fmaf(bf16_lo(x), bf16_lo(y), acc);
+      acc = fmaf(bf16_hi(x), bf16_hi(y), acc);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (sub == 0 && row < rows) {
+    const int64_t t = row / Hq, h = row % Hq;
+    delta[h * T + t] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------- dQ --
+
+constexpr int Q_KT = PG_KEY_TILE;            // 64 keys per tile
+constexpr int Q_QW = PG_WAVE_QUERIES;        // 32 query rows per wave
+constexpr int Q_WAVES = PG_ITEM_WAVES;       // 8 waves, as the forward's items
+constexpr int Q_REGION = Q_KT * D * 2;       // 16 KB
+constexpr int Q_STAGE = 3 * Q_REGION;        // K row-major, V row-major, K for transposing reads
+constexpr int Q_NSTAGE = 3;
+constexpr int Q_LOADS = 6;                   // 1 KB loads per wave per tile
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* delta;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const pg_work_item* items;
+  const pg_key_span* spans;
+  const int32_t* tok_ss;
+  const pg_kv_item* kv_items;
+  int32_t T, Hq, Hkv, r, hpw;
+  float c_log2;   // softmax_scale * log2(e)
+  float scale;
+};
+
+// Walks the 64-key tiles of an item's key spans (scalar state).
+struct SpanTiles {
+  int s, s_end, ka, k0, k1;
+  __device__ void load(const pg_key_span* spans) {
+    k0 = ld_scalar(spans, 2 * s);
+    k1 = ld_scalar(spans, 2 * s + 1);
+    ka = k0;
+  }
+  __device__ void init(const pg_key_span* spans, int s0, int n) {
+    s = __builtin_amdgcn_readfirstlane(s0);
+    s_end = __builtin_amdgcn_readfirstlane(s0 + n);
+    load(spans);
+  }
+  __device__ void next(const pg_key_span* spans) {
+    ka += Q_KT;
+    if (ka >= k1 && ++s < s_end) load(spans);
+  }
+};
+
+__global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Q_NSTAGE * Q_STAGE];
+
+  const pg_work_item it = a.items[blockIdx.x];
+  if (it.nspan == 0) return;   // padding of a shorter XCD queue
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qi = lane & 31;
+  const int half = lane >> 5;
+
+  const int h = it.hq0 + wave % a.hpw;
+  const int hk = it.hq0 / a.r;
+  const int tb = it.t0 + Q_QW * (wave / a.hpw);
+  const int te = min(tb + Q_QW, it.t1);
+  const bool wave_active = tb < te;
+  const int tq = wave_active ? min(tb + qi, te - 1) : it.t0;
+  const bool row_valid = wave_active && (tb + qi < te);
+
+  // Q and dO rows as B operands (lane: query qi, d = 16 ks + 8 half + 0..7)
+  bf16x8_t qf[8], dof[8];
+  {
+    const int64_t base = (int64_t(tq) * a.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = as_bf16x8(ldg16(a.q + base + 16 * ks));
+      dof[ks] = as_bf16x8(ldg16(a.dout + base + 16 * ks));
+    }
+  }
+  const float lse2 = a.lse[int64_t(h) * a.T + tq] * LOG2E;
+  const float dlt = a.delta[int64_t(h) * a.T + tq];
+  const int ss_t = a.tok_ss[tq];
+  const int ss_max = ld_scalar(a.tok_ss, wave_active ? te - 1 : it.t0);
+
+  int ntiles = 0;
+  for (int s = it.span0; s < it.span0 + it.nspan; ++s)
+    ntiles += (ld_scalar(a.spans, 2 * s + 1) - ld_scalar(a.spans, 2 * s) + Q_KT - 1) / Q_KT;
+
+  // staging: waves 0-3 bring K row-major (blocks 4 w + i) and the first half
+  // of K for transposing reads (blocks 2 w + i); waves 4-7 bring V row-major
+  // and the second half.
+  const int w4 = wave & 3;
+  const bool vgrp = wave >= 4;
+  const int kv_row_bytes = a.Hkv * D * 2;
+  int goff[Q_LOADS];
+  uint32_t ldst[Q_LOADS];
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    goff[i] = rowmajor_off(4 * w4 + i, lane, kv_row_bytes);
+    ldst[i] = (vgrp ? Q_REGION : 0) + 1024 * (4 * w4 + i);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = (vgrp ? 8 : 0) + 2 * w4 + i;
+    goff[4 + i] = trread_off(b, lane, kv_row_bytes);
+    ldst[4 + i] = 2 * Q_REGION + 1024 * b;
+  }
+  auto fetch = [&](int ka, int k1, int stage) {
+    ka = __builtin_amdgcn_readfirstlane(ka);
+    k1 = __builtin_amdgcn_readfirstlane(k1);
+    const int bytes = (k1 - ka - 1) * kv_row_bytes + D * 2;
+    const int64_t row0 = (int64_t(ka) * a.Hkv + hk) * D;
+    const i32x4_t rk = make_rsrc(a.k + row0, bytes);
+    const i32x4_t rrm = vgrp ? make_rsrc(a.v + row0, bytes) : rk;
+    const uint32_t sb = lds_base + uint32_t(stage * Q_STAGE);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf16_to_lds(rrm, goff[i], sb + ldst[i]);
+#pragma unroll
+    for (int i = 4; i < Q_LOADS; ++i) buf16_to_lds(rk, goff[i], sb + ldst[i]);
+  };
+
+  // A operand reads: row-major K/V row 32 kb + qi, chunk 2 ks + half (swizzled)
+  int koff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * 256 + 16 * ((2 * ks + half) ^ (qi & 15));
+  const int troff = 2 * Q_REGION + 8 * lane;
+
+  f32x16_t dqacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+  SpanTiles ld, cp;
+  ld.init(a.spans, it.span0, it.nspan);
+  fetch(ld.ka, ld.k1, 0);
+  ld.next(a.spans);
+  if (ntiles > 1) {
+    fetch(ld.ka, ld.k1, 1);
+    ld.next(a.spans);
+  }
+  cp.init(a.spans, it.span0, it.nspan);
+
+  for (int n = 0; n < ntiles; ++n) {
+    // tile n landed (tile n + 1 may still be in flight); after the barrier
+    // every wave is done with tile n - 1, whose stage tile n + 2 takes
+    if (n + 1 < ntiles)
+      wait_vmem<Q_LOADS>();
+    else
+      wait_vmem<0>();
+    bare_barrier();
+    if (n + 2 < ntiles) {
+      fetch(ld.ka, ld.k1, (n + 2) % Q_NSTAGE);
+      ld.next(a.spans);
+    }
+    const int ka = cp.ka, k1 = cp.k1;
+    const bool is_prefix = k1 <= it.pe;
+    bool part = wave_active && ka <= te - 1;
+    if (!is_prefix) part = part && (__ballot(row_valid && ss_t == cp.k0) != 0ull);
+    const bool full = (ka + Q_KT <= k1) && (ka + Q_KT - 1 <= tb) && (is_prefix || ss_max <= ka);
+    cp.next(a.spans);
+    if (!part) continue;
+    const unsigned char* st = smem + (n % Q_NSTAGE) * Q_STAGE;
+
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[0][i] = 0.f;
+      sacc[1][i] = 0.f;
+      pacc[0][i] = 0.f;
+      pacc[1][i] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t ak = as_bf16x8(*reinterpret_cast<const uint4*>(st + 8192 * kb + koff[ks]));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], sacc[kb], 0, 0, 0);
+      }
+    sched_reads_ahead<4, 1, 16>();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t av =
+            as_bf16x8(*reinterpret_cast<const uint4*>(st + Q_REGION + 8192 * kb + koff[ks]));
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], pacc[kb], 0, 0, 0);
+      }
+    sched_reads_ahead<4, 1, 16>();
+
+    // P^T and dS^T; register i of block kb holds key ka + 32 kb + 8 (i/4) + 4 half + i%4
+    const int base = ka + 4 * half;
+    const int lo = (is_prefix ? ka : ss_t) - base;
+    const int hi = min(tq, k1 - 1) - base;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = 32 * kb + 8 * (i >> 2) + (i & 3);
+        float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -lse2));
+        if (!full) p = (c >= lo && c <= hi) ? p : 0.f;
+        sacc[kb][i] = p * (pacc[kb][i] - dlt);
+      }
+    bf16x8_t dsf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) dsf[ks] = pack_step(sacc[ks >> 1], ks);
+
+    // dQ^T += K^T dS^T
+    const unsigned char* vb = st + troff;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(vb, ks, db), dsf[ks],
+                                                            dqacc[db], 0, 0, 0);
+    sched_reads_ahead<6, 2, 16>();
+  }
+
+  // every wave is done with the ring before it holds the output tiles
+  wait_vmem<0>();
+  __syncthreads();
+  if (wave_active)
+    store_tile<false>(dqacc, a.scale, smem + 8192 * wave, lane,
+                      a.dq + (int64_t(tb) * a.Hq + h) * D, int64_t(a.Hq) * D, te - tb);
+}
+
+// ------------------------------------------------------------------ dK, dV --
+
+constexpr int KV_QT = 32;                    // query rows per tile
+constexpr int KV_WAVES = 4;                  // 32 keys each (PG_KV_BLOCK = 128)
+constexpr int KV_REGION = KV_QT * D * 2;     // 8 KB
+constexpr int KV_ROWS = 4 * KV_REGION;       // Q, dO row-major; Q, dO for transposing reads
+constexpr int KV_STAGE = KV_ROWS + 3 * 256;  // + lse, D, and a sink for unused lanes' loads
+constexpr int KV_NSTAGE = 3;
+constexpr int KV_LOADS = 9;                  // per wave per tile: 8 x 1 KB + one 256 B load
+
+static_assert(KV_WAVES * 32 == PG_KV_BLOCK, "key block = waves x 32 keys");
+
+__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[KV_NSTAGE * KV_STAGE];
+
+  const pg_kv_item it = a.kv_items[blockIdx.x];
+  if (it.k1 <= it.k0) return;   // padding
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;    // key of this lane inside the wave's 32
+  const int half = lane >> 5;
+
+  const int hk = it.hk;
+  const int kw0 = it.k0 + 32 * wave;
+  const int kw1 = min(kw0 + 32, it.k1);
+  const bool wave_keys = kw0 < kw1;
+  const int key = kw0 + col;
+  const bool key_valid = key < kw1;
+
+  // K and V rows of the wave's keys as B operands (lane: key col,
+  // d = 16 ks + 8 half + 0..7); keys past the block read as zeros
+  bf16x8_t kf[8], vf[8];
+  {
+    const int64_t base = (int64_t(key_valid ? key : it.k0) * a.Hkv + hk) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 zk = key_valid ? ldg16(a.k + base + 16 * ks) : make_uint4(0, 0, 0, 0);
+      const uint4 zv = key_valid ? ldg16(a.v + base + 16 * ks) : make_uint4(0, 0, 0, 0);
+      kf[ks] = as_bf16x8(zk);
+      vf[ks] = as_bf16x8(zv);
+    }
+  }
+
+  f32x16_t dkacc[4], dvacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  // query tiles: rows q0 = k0 + 32 m (m < nq) for each query head of hk
+  const int q_start = it.k0;
+  const int nq = (it.qend - q_start + KV_QT - 1) / KV_QT;
+  const int ntiles = nq * a.r;
+  const int q_row_bytes = a.Hq * D * 2;
+
+  // staging: wave w brings blocks 2 w, 2 w + 1 of each 8 KB region
+  // (Q, dO row-major; Q, dO for transposing reads) and one 256 B row:
+  // wave 0 lse, wave 1 D, waves 2-3 an empty load into the sink
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
+  int goff[8];
+  uint32_t ldst[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = 2 * wave + i;
+    goff[0 + i] = rowmajor_off(b, lane, q_row_bytes);           // Q row-major
+    ldst[0 + i] = 0 * KV_REGION + 1024 * b;
+    goff[2 + i] = goff[0 + i];                                  // dO row-major
+    ldst[2 + i] = 1 * KV_REGION + 1024 * b;
+    goff[4 + i] = trread_off(b, lane, q_row_bytes);             // Q transposing
+    ldst[4 + i] = 2 * KV_REGION + 1024 * b;
+    goff[6 + i] = goff[4 + i];                                  // dO transposing
+    ldst[6 + i] = 3 * KV_REGION + 1024 * b;
+  }
+  auto fetch = [&](int n, int stage) {
+    const int m = n / a.r, h = hk * a.r + n % a.r;
+    const int q0 = q_start + KV_QT * m;
+    const int rows = min(KV_QT, it.qend - q0);
+    const int bytes = (rows - 1) * q_row_bytes + D * 2;
+    const int64_t row0 = (int64_t(q0) * a.Hq + h) * D;
+    const i32x4_t rq = make_rsrc(a.q + row0, bytes);
+    const i32x4_t rd = make_rsrc(a.dout + row0, bytes);
+    const uint32_t sb = lds_base + uint32_t(stage * KV_STAGE);
+    buf16_to_lds(rq, goff[0], sb + ldst[0]);
+    buf16_to_lds(rq, goff[1], sb + ldst[1]);
+    buf16_to_lds(rd, goff[2], sb + ldst[2]);
+    buf16_to_lds(rd, goff[3], sb + ldst[3]);
+    buf16_to_lds(rq, goff[4], sb + ldst[4]);
+    buf16_to_lds(rq, goff[5], sb + ldst[5]);
+    buf16_to_lds(rd, goff[6], sb + ldst[6]);
+    buf16_to_lds(rd, goff[7], sb + ldst[7]);
+    // the tile's 32 lse (wave 0) or D (wave 1) values; lanes past the rows
+    // read zeros
+    const float* src = wave == 0 ? a.lse : a.delta;
+    const i32x4_t rl = make_rsrc(src + int64_t(h) * a.T + q0, wave < 2 ? 4 * rows : 0);
+    buf4_to_lds(rl, 4 * lane, sb + KV_ROWS + 256 * min(wave, 2));
+  };
+
+  // A operand reads of row-major Q / dO: row col, chunk 2 ks + half (swizzled)
+  int aoff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) aoff[ks] = col * 256 + 16 * ((2 * ks + half) ^ (col & 15));
+
+  fetch(0, 0);
+  if (ntiles > 1) fetch(1, 1);
+
+  for (int n = 0; n < ntiles; ++n) {
+    if (n + 1 < ntiles)
+      wait_vmem<KV_LOADS>();
+    else
+      wait_vmem<0>();
+    bare_barrier();
+    if (n + 2 < ntiles) fetch(n + 2, (n + 2) % KV_NSTAGE);
+    if (!wave_keys) continue;
+    const int q0 = q_start + KV_QT * (n / a.r);
+    // rows of this tile that can read any of the wave's keys
+    if (q0 + KV_QT - 1 < kw0) continue;
+    const unsigned char* st = smem + (n % KV_NSTAGE) * KV_STAGE;
+
+    f32x16_t sacc, pacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] = 0.f;
+      pacc[i] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t aq = as_bf16x8(*reinterpret_cast<const uint4*>(st + aoff[ks]));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t ad = as_bf16x8(*reinterpret_cast<const uint4*>(st + KV_REGION + aoff[ks]));
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], pacc, 0, 0, 0);
+    }
+    sched_reads_ahead<4, 1, 16>();
+
+    // register i holds query row q0 + 8 (i/4) + 4 half + i%4 of key `key`
+    const float* lse_t = reinterpret_cast<const float*>(st + KV_ROWS);
+    const float* dlt_t = reinterpret_cast<const float*>(st + KV_ROWS + 256);
+    const bool full = (q0 >= kw0 + 31) && (q0 + KV_QT <= it.qend);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = 8 * g + 4 * half;
+      const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
+      const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + r0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        const int qrow = q0 + r0 + j;
+        float p = fast_exp2(fmaf(sacc[i], a.c_log2, -(&l4.x)[j] * LOG2E));
+        if (!full) p = (qrow >= key && qrow < it.qend) ? p : 0.f;
+        pacc[i] = p * (pacc[i] - (&d4.x)[j]);   // dS
+        sacc[i] = p;                            // P
+      }
+    }
+    bf16x8_t pf[2], dsf[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      pf[s] = pack_step(sacc, s);
+      dsf[s] = pack_step(pacc, s);
+    }
+    // dV += P^T dO, dK += dS^T Q (B by transposing reads of dO, Q)
+    const unsigned char* vq = st + 2 * KV_REGION + 8 * lane;
+    const unsigned char* vd = st + 3 * KV_REGION + 8 * lane;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[s], tr_operand(vd, s, db),
+                                                            dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[s], tr_operand(vq, s, db),
+                                                            dkacc[db], 0, 0, 0);
+      }
+    sched_reads_ahead<8, 2, 16>();
+  }
+
+  wait_vmem<0>();
+  __syncthreads();
+  if (wave_keys) {
+    unsigned char* ot = smem + 16384 * wave;
+    const int64_t rs = int64_t(a.Hkv) * D;
+    store_tile<true>(dvacc, 1.f, ot, lane, a.dv + (int64_t(kw0) * a.Hkv + hk) * D, rs, kw1 - kw0);
+    store_tile<true>(dkacc, a.scale, ot + 8192, lane, a.dk + (int64_t(kw0) * a.Hkv + hk) * D, rs,
+                     kw1 - kw0);
+  }
+}
+
+}  // namespace
+
+hipError_t pg_launch_attn_bwd(const pg_layout& L, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dout, void* dq,
+                              void* dk, void* dv, float* delta, float softmax_scale,
+                              hipStream_t stream) {
+  if (L.items.empty()) return hipSuccess;
+  const int64_t rows = L.T * L.Hq;
+  bwd_delta_kernel<<<dim3(uint32_t((rows + 15) / 16)), dim3(256), 0, stream>>>(
+      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), delta, int(L.T), L.Hq);
+  BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.items = L.d_items;
+  a.spans = L.d_spans;
+  a.tok_ss = L.d_ss;
+  a.kv_items = L.d_kv_items;
+  a.T = int32_t(L.T);
+  a.Hq = L.Hq;
+  a.Hkv = L.Hkv;
+  a.r = L.Hq / L.Hkv;
+  a.hpw = L.heads_per_item;
+  a.c_log2 = softmax_scale * LOG2E;
+  a.scale = softmax_scale;
+  bwd_dq_kernel<<<dim3(uint32_t(L.items.size())), dim3(64 * Q_WAVES), 0, stream>>>(a);
+  if (!L.kv_items.empty())
+    bwd_dkv_kernel<<<dim3(uint32_t(L.kv_items.size())), dim3(64 * KV_WAVES), 0, stream>>>(a);
+  return hipGetLastError();
+}

@@ -100,7 +100,8 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   const size_t off_it = align_up(off_ss + 4 * T, A);
   const size_t off_sp = align_up(off_it + sizeof(pg_work_item) * L->items.size(), A);
   const size_t off_fr = align_up(off_sp + sizeof(pg_key_span) * L->spans.size(), A);
-  const size_t bytes = align_up(off_fr + sizeof(double) * L->inv_freq.size(), A);
+  const size_t off_kv = align_up(off_fr + sizeof(double) * L->inv_freq.size(), A);
+  const size_t bytes = align_up(off_kv + sizeof(pg_kv_item) * L->kv_items.size(), A);
   hipError_t e = hipGetDevice(&L->device);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   pg_slot* slot = nullptr;
@@ -115,6 +116,8 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   if (!L->spans.empty())
     std::memcpy(h + off_sp, L->spans.data(), sizeof(pg_key_span) * L->spans.size());
   std::memcpy(h + off_fr, L->inv_freq.data(), sizeof(double) * L->inv_freq.size());
+  if (!L->kv_items.empty())
+    std::memcpy(h + off_kv, L->kv_items.data(), sizeof(pg_kv_item) * L->kv_items.size());
   void* d = slot->dev;
   e = hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) {
@@ -131,6 +134,7 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   L->d_items = reinterpret_cast<const pg_work_item*>(b + off_it);
   L->d_spans = reinterpret_cast<const pg_key_span*>(b + off_sp);
   L->d_inv_freq = reinterpret_cast<const double*>(b + off_fr);
+  L->d_kv_items = reinterpret_cast<const pg_kv_item*>(b + off_kv);
   return PG_OK;
 }
 
@@ -165,6 +169,8 @@ pg_status pg_layout_info(const pg_layout* L, pg_layout_summary* info) {
   info->max_item_cost = L->max_item_cost;
   info->max_xcd_cost = 0;
   for (int64_t c : L->xcd_load) info->max_xcd_cost = c > info->max_xcd_cost ? c : info->max_xcd_cost;
+  info->num_kv_items = int32_t(L->kv_items.size());
+  info->reserved = 0;
   return PG_OK;
 }
 
@@ -190,6 +196,13 @@ pg_status pg_layout_copy_work(const pg_layout* L, pg_work_item* items, pg_key_sp
     std::memcpy(items, L->items.data(), sizeof(pg_work_item) * L->items.size());
   if (spans && !L->spans.empty())
     std::memcpy(spans, L->spans.data(), sizeof(pg_key_span) * L->spans.size());
+  return PG_OK;
+}
+
+pg_status pg_layout_copy_kv_work(const pg_layout* L, pg_kv_item* items) {
+  if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
+  if (items && !L->kv_items.empty())
+    std::memcpy(items, L->kv_items.data(), sizeof(pg_kv_item) * L->kv_items.size());
   return PG_OK;
 }
 
@@ -240,6 +253,28 @@ pg_status pg_attn_fwd(const pg_layout* L, const void* q, const void* k, const vo
     e = pg_launch_attn_rowwise(*L, q, k, v, o, lse, dtype, softmax_scale, stream);
   pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "attention kernel launch");
+}
+
+pg_status pg_attn_bwd(const pg_layout* L, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                      void* dv, float* delta, pg_dtype dtype, float softmax_scale,
+                      hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (dtype != PG_BF16 || L->d != 128)
+    return pg_fail(PG_ERR_UNSUPPORTED, "backward needs bf16 and head_dim 128 (dtype %d, d %d)",
+                   int(dtype), L->d);
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return pg_fail(PG_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (L->T == 0) return PG_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta)
+    return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (dq == dk || dq == dv || dk == dv)
+    return pg_fail(PG_ERR_INVALID_ARG, "dq, dk, dv must be distinct buffers");
+  hipError_t e = pg_launch_attn_bwd(*L, q, k, v, o, lse, dout, dq, dk, dv, delta, softmax_scale,
+                                    stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "backward kernel launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,123 @@
+// Device helpers shared by the attention kernels of libpg.so (forward and
+// backward): operand types, buffer->LDS loads, transposing LDS reads, bf16
+// packing, wait counters and MFMA/LDS-read scheduling patterns. gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pg_hip {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (four SGPRs) over `bytes` bytes from `base`: 48-bit base,
+// stride 0, num_records = bytes, gfx9 dword3 = untyped 32-bit data. Loads at
+// or past `bytes` return zeros, so rows past the end of a key span need no
+// clamping. Every field must be wave-uniform.
+__device__ inline i32x4_t make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(p)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from buffer `r` at byte offset `voff` straight into LDS at
+// byte address lds + 16 * lane (lds is wave-uniform). Written as asm so the
+// compiler does not guard every later LDS read with a full vmcnt(0) wait: the
+// loads only write LDS (no VGPR result), and their completion is awaited
+// explicitly (wait_vmem_*) before the barrier that publishes the tile. M0 is
+// written here, one wait state before the load that reads it; the compiler
+// keeps no value in M0 across these kernels' code (no M0-relative LDS
+// instruction is used, checked in the generated code).
+__device__ inline void buf16_to_lds(i32x4_t r, int voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(lds)
+      : "memory");
+}
+
+__device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Transposing LDS read: inside each group of 16 lanes, lane d receives element
+// d % 4 of the 8-byte chunks addressed by lanes 4 j + d / 4, j = 0..3.
+__device__ inline i16x4_t lds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  // nearest-even fp32 -> bf16 of two values in one v_cvt_pk_bf16_f32
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane l ^ 32 (the other half of the wave), through a VALU lane swap
+// instead of an LDS round trip.
+__device__ inline float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // r[0] holds lanes 0-31 in both halves, r[1] lanes 32-63 in both halves
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Wave-uniform int from read-only global memory, as a scalar load.
+__device__ inline int ld_scalar(const void* base, int i) {
+  const __attribute__((address_space(4))) int* c = (const __attribute__((address_space(4))) int*)(base);
+  return __builtin_amdgcn_readfirstlane(c[i]);
+}
+
+// s_waitcnt vmcnt(N) for N < 16 (gfx9 encoding: expcnt and lgkmcnt fields
+// left at "no wait").
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt fields at "no wait").
+__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier alone (no memory fence: loads may stay in flight). The
+// memory clobber keeps the compiler from moving memory operations across; the
+// scheduling barriers keep arithmetic on its side.
+__device__ inline void bare_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scheduling pattern for a block of NM MFMAs fed by LDS reads: AHEAD reads
+// first, then PER reads after each MFMA until the reads run out.
+template <int I, int NM, int PER, int REST>
+__device__ inline void sched_mfma_then_reads() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    constexpr int r = REST >= PER ? PER : REST;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);   // r LDS reads
+    sched_mfma_then_reads<I + 1, NM, PER, REST - r>();
+  }
+}
+template <int AHEAD, int PER, int NM>
+__device__ inline void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+  sched_mfma_then_reads<0, NM, PER, NM * PER - AHEAD>();
+}
+
+}  // namespace pg_hip

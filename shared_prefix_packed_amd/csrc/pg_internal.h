@@ -55,6 +55,7 @@ struct pg_layout {
   std::vector<pg_key_span> spans;
   int64_t max_item_cost = 0;
   std::vector<int64_t> xcd_load;   // summed item cost per XCD queue
+  std::vector<pg_kv_item> kv_items;   // backward (dK, dV) work list, launch order
 
   // device copy (one upload slot, filled by pg_layout_upload)
   int device = -1;
@@ -66,6 +67,7 @@ struct pg_layout {
   const pg_work_item* d_items = nullptr;
   const pg_key_span* d_spans = nullptr;
   const double* d_inv_freq = nullptr;
+  const pg_kv_item* d_kv_items = nullptr;
 };
 
 // Host layout builder (pg_layout.cpp). Validates and fills `L`.
@@ -87,6 +89,10 @@ hipError_t pg_launch_rope(const pg_layout& L, const int64_t* pos, const void* q_
 hipError_t pg_launch_attn_rowwise(const pg_layout& L, const void* q, const void* k,
                                   const void* v, void* o, float* lse, pg_dtype dtype,
                                   float softmax_scale, hipStream_t stream);
+hipError_t pg_launch_attn_bwd(const pg_layout& L, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dout, void* dq,
+                              void* dk, void* dv, float* delta, float softmax_scale,
+                              hipStream_t stream);
 hipError_t pg_launch_attn_mfma(const pg_layout& L, const void* q, const void* k, const void* v,
                                void* o, float* lse, float softmax_scale, hipStream_t stream);
 
@@ -95,3 +101,4 @@ constexpr int PG_WAVE_QUERIES = 32;   // query tokens per wave in the MFMA kerne
 constexpr int PG_ITEM_WAVES = 8;      // waves per work item (workgroup): two ping-pong groups of 4
 constexpr int PG_KEY_TILE = 64;       // keys per LDS tile
 constexpr int PG_XCDS = 8;            // XCDs of an MI355X; workgroup p runs on XCD p % 8
+constexpr int PG_KV_BLOCK = 128;      // keys per backward dK/dV work item (4 waves x 32)

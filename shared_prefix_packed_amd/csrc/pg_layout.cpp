@@ -36,6 +36,54 @@ inline int64_t keys_of(int32_t t, int32_t g0, int32_t pe, int32_t ss) {
   return int64_t(pe - g0) + int64_t(t - ss + 1);
 }
 
+// Launch order over the XCDs. Workgroups are dispatched round-robin over the
+// XCDs (workgroup p runs on XCD p % 8), and each XCD has its own L2. All items
+// of one cluster (same group and KV head) read the same K/V (forward) or Q/dO
+// (backward), so a cluster is placed on one XCD: clusters go to the XCD with
+// the least load so far, largest first (LPT over cluster costs); inside an XCD,
+// clusters run largest first and the items of a cluster in the order `before`
+// gives, so each XCD's queue is in LPT order and the cluster's shared rows stay
+// hot in its L2. Returns item indices by launch position, -1 where an XCD
+// whose queue ran out needs a padding item; trailing padding is dropped.
+template <class Before>
+std::vector<int32_t> xcd_launch_order(const std::vector<int64_t>& cost,
+                                      const std::vector<int64_t>& cluster, int64_t ncl,
+                                      Before before, std::vector<int64_t>* xcd_load_out) {
+  std::vector<int64_t> cl_cost(static_cast<size_t>(ncl), 0);
+  std::vector<std::vector<int32_t>> cl_items(static_cast<size_t>(ncl));
+  for (size_t i = 0; i < cost.size(); ++i) {
+    cl_cost[size_t(cluster[i])] += cost[i];
+    cl_items[size_t(cluster[i])].push_back(int32_t(i));
+  }
+  std::vector<int64_t> order;
+  for (int64_t c = 0; c < ncl; ++c)
+    if (!cl_items[size_t(c)].empty()) order.push_back(c);
+  std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+    return cl_cost[size_t(a)] > cl_cost[size_t(b)];
+  });
+  std::vector<int64_t> xcd_load(PG_XCDS, 0);
+  std::vector<std::vector<int32_t>> xcd_queue(PG_XCDS);
+  for (int64_t c : order) {
+    int x = 0;
+    for (int j = 1; j < PG_XCDS; ++j)
+      if (xcd_load[j] < xcd_load[x]) x = j;
+    xcd_load[x] += cl_cost[size_t(c)];
+    std::vector<int32_t>& its = cl_items[size_t(c)];
+    std::stable_sort(its.begin(), its.end(), before);
+    xcd_queue[x].insert(xcd_queue[x].end(), its.begin(), its.end());
+  }
+  size_t rows = 0;
+  for (const auto& qx : xcd_queue) rows = std::max(rows, qx.size());
+  std::vector<int32_t> launch;
+  launch.reserve(rows * PG_XCDS);
+  for (size_t i = 0; i < rows; ++i)
+    for (int x = 0; x < PG_XCDS; ++x)
+      launch.push_back(i < xcd_queue[x].size() ? xcd_queue[x][i] : -1);
+  while (!launch.empty() && launch.back() < 0) launch.pop_back();
+  if (xcd_load_out) *xcd_load_out = xcd_load;
+  return launch;
+}
+
 }  // namespace
 
 pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* prefix_lens,
@@ -187,61 +235,73 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
       seg += 1 + nseg;
       k += nseg;
     }
-    // Launch order. Workgroups are dispatched round-robin over the XCDs
-    // (workgroup p runs on XCD p % 8), and each XCD has its own L2. All items
-    // of one (group, KV head) cluster read the same prefix K/V, so a cluster is
-    // placed on one XCD: clusters go to the XCD with the least load so far,
-    // largest first (LPT over cluster costs); inside an XCD, clusters run
-    // largest first and the items of a cluster largest first, so each XCD's
-    // own queue is in LPT order and the cluster's prefix stays hot in its L2.
-    // Positions of XCDs whose queue ran out are padded with empty items
-    // (nspan = 0), which the kernel leaves at once.
-    const int64_t ncl = int64_t(num_groups) * num_kv_heads;
-    std::vector<int64_t> cl_cost(static_cast<size_t>(ncl), 0);
-    std::vector<std::vector<int32_t>> cl_items(static_cast<size_t>(ncl));
+    // Launch order: see xcd_launch_order.
+    std::vector<int64_t> costs(L.items.size()), clusters(L.items.size());
     for (size_t i = 0; i < L.items.size(); ++i) {
-      const pg_work_item& it = L.items[i];
-      const int64_t c = int64_t(item_group[i]) * num_kv_heads + it.hq0 / r;
-      cl_cost[size_t(c)] += it.cost;
-      cl_items[size_t(c)].push_back(int32_t(i));
+      costs[i] = L.items[i].cost;
+      clusters[i] = int64_t(item_group[i]) * num_kv_heads + L.items[i].hq0 / r;
     }
-    std::vector<int64_t> order;
-    for (int64_t c = 0; c < ncl; ++c)
-      if (!cl_items[size_t(c)].empty()) order.push_back(c);
-    std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
-      return cl_cost[size_t(a)] > cl_cost[size_t(b)];
-    });
-    std::vector<int64_t> xcd_load(PG_XCDS, 0);
-    std::vector<std::vector<int32_t>> xcd_queue(PG_XCDS);
-    for (int64_t c : order) {
-      int x = 0;
-      for (int j = 1; j < PG_XCDS; ++j)
-        if (xcd_load[j] < xcd_load[x]) x = j;
-      xcd_load[x] += cl_cost[size_t(c)];
-      std::vector<int32_t>& its = cl_items[size_t(c)];
-      std::stable_sort(its.begin(), its.end(), [&](int32_t a, int32_t b) {
-        const pg_work_item &ia = L.items[size_t(a)], &ib = L.items[size_t(b)];
-        if (ia.cost != ib.cost) return ia.cost > ib.cost;
-        if (ia.t0 != ib.t0) return ia.t0 < ib.t0;
-        return ia.hq0 < ib.hq0;
-      });
-      xcd_queue[x].insert(xcd_queue[x].end(), its.begin(), its.end());
-    }
-    size_t rows = 0;
-    for (const auto& qx : xcd_queue) rows = std::max(rows, qx.size());
+    std::vector<int64_t> xcd_load;
+    const std::vector<int32_t> pos = xcd_launch_order(
+        costs, clusters, int64_t(num_groups) * num_kv_heads,
+        [&](int32_t a, int32_t b) {
+          const pg_work_item &ia = L.items[size_t(a)], &ib = L.items[size_t(b)];
+          if (ia.cost != ib.cost) return ia.cost > ib.cost;
+          if (ia.t0 != ib.t0) return ia.t0 < ib.t0;
+          return ia.hq0 < ib.hq0;
+        },
+        &xcd_load);
     std::vector<pg_work_item> launch;
-    launch.reserve(rows * PG_XCDS);
+    launch.reserve(pos.size());
     pg_work_item empty{};
-    empty.pe = 0;
-    empty.nspan = 0;
-    empty.cost = 0;
-    for (size_t i = 0; i < rows; ++i)
-      for (int x = 0; x < PG_XCDS; ++x)
-        launch.push_back(i < xcd_queue[x].size() ? L.items[size_t(xcd_queue[x][i])] : empty);
-    // drop trailing empty items
-    while (!launch.empty() && launch.back().nspan == 0) launch.pop_back();
+    for (int32_t i : pos) launch.push_back(i >= 0 ? L.items[size_t(i)] : empty);
     L.items.swap(launch);
     L.xcd_load = xcd_load;
+
+    // Backward work list (dK, dV): blocks of PG_KV_BLOCK keys of one KV head
+    // that never cross a segment. The queries that read key j form one
+    // contiguous range [j, qend): a prompt key is read by every later token of
+    // its group (the rest of the prompt and all responses), a response key by
+    // the rest of its own response. qend is the group end or the response end.
+    std::vector<pg_kv_item> kv;
+    std::vector<int64_t> kv_cluster;
+    {
+      int32_t sg = 0;   // index of the group's prefix segment in seg_off
+      for (int32_t g = 0; g < num_groups; ++g) {
+        const int32_t nseg = suffix_counts[g];
+        const int32_t gend = L.group_off[g + 1];
+        for (int32_t j = 0; j <= nseg; ++j) {
+          const int32_t a = L.seg_off[sg + j], b = L.seg_off[sg + j + 1];
+          const int32_t qend = j == 0 ? gend : b;
+          for (int32_t k0 = a; k0 < b; k0 += PG_KV_BLOCK) {
+            const int32_t k1 = std::min<int32_t>(k0 + PG_KV_BLOCK, b);
+            const int64_t n = k1 - k0;
+            // sum over keys of the queries reading them, times the r query heads
+            const int64_t pairs = n * int64_t(qend) - (int64_t(k0) + k1 - 1) * n / 2;
+            for (int32_t hk = 0; hk < num_kv_heads; ++hk) {
+              kv.push_back(pg_kv_item{k0, k1, hk, qend, pairs * r});
+              kv_cluster.push_back(int64_t(g) * num_kv_heads + hk);
+            }
+          }
+        }
+        sg += 1 + nseg;
+      }
+      std::vector<int64_t> kv_cost(kv.size());
+      for (size_t i = 0; i < kv.size(); ++i) kv_cost[i] = kv[i].cost;
+      const std::vector<int32_t> kpos = xcd_launch_order(
+          kv_cost, kv_cluster, int64_t(num_groups) * num_kv_heads,
+          [&](int32_t a, int32_t b) {
+            const pg_kv_item &ia = kv[size_t(a)], &ib = kv[size_t(b)];
+            if (ia.cost != ib.cost) return ia.cost > ib.cost;
+            if (ia.k0 != ib.k0) return ia.k0 < ib.k0;
+            return ia.hk < ib.hk;
+          },
+          nullptr);
+      L.kv_items.clear();
+      L.kv_items.reserve(kpos.size());
+      for (int32_t i : kpos)
+        L.kv_items.push_back(i >= 0 ? kv[size_t(i)] : pg_kv_item{0, 0, 0, 0, 0});
+    }
   } catch (const std::bad_alloc&) {
     return pg_fail(PG_ERR_OOM, "host allocation failed");
   }

@@ -252,3 +252,62 @@ def test_empty_layout_is_a_no_op():
     assert s.total_tokens == 0 and s.num_items == 0 and s.max_position == -1
     L2 = _build([0, 0], [[0], []])
     assert L2.summary().total_tokens == 0
+
+
+# ------------------------------------------------------ backward work list --
+
+def _check_kv_invariants(L, P, S, hq, hkv):
+    n, flat = _flat(S)
+    lay = O.layout(P, n, flat)
+    T = lay["total_tokens"]
+    r = hq // hkv
+    grp, seg, _ = O.segment_ids(lay)
+    # readers of each key, counted from the oracle's key sets
+    readers = np.zeros(T, dtype=np.int64)
+    last_reader = np.full(T, -1, dtype=np.int64)
+    for t in range(T):
+        for j in O.allowed_keys(lay, t):
+            readers[j] += 1
+            last_reader[j] = max(last_reader[j], t)
+    kv = L.kv_work()
+    assert L.summary().num_kv_items == kv.size
+    cover = np.zeros((T, hkv), dtype=np.int64)
+    xcd_of_cluster = {}
+    for p, it in enumerate(kv):
+        k0, k1, hk, qend = int(it["k0"]), int(it["k1"]), int(it["hk"]), int(it["qend"])
+        if k1 <= k0:
+            assert it["cost"] == 0
+            continue
+        assert k1 - k0 <= 128 and 0 <= hk < hkv
+        assert grp[k0] == grp[k1 - 1] and seg[k0] == seg[k1 - 1], "block crosses a segment"
+        cover[k0:k1, hk] += 1
+        # every reader of these keys lies in [k0, qend), and qend is reached
+        assert last_reader[k0:k1].max() == qend - 1
+        assert it["cost"] == readers[k0:k1].sum() * r
+        cl = (int(grp[k0]), hk)
+        assert xcd_of_cluster.setdefault(cl, p % 8) == p % 8
+    assert (cover == 1).all(), "every (key, KV head) in exactly one block"
+    assert kv.size == 0 or kv[-1]["k1"] > kv[-1]["k0"], "no trailing padding"
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("heads", [(4, 1), (32, 8), (6, 2)])
+def test_backward_work_list_invariants(shape, heads):
+    P, S = shape
+    L = _build(P, S, hq=heads[0], hkv=heads[1])
+    _check_kv_invariants(L, P, S, *heads)
+
+
+def test_backward_work_list_on_dpo_workload():
+    w = make_workload(1)
+    L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens, 32, 8, 128, 5e5)
+    _check_kv_invariants(L, w.prefix_lens.tolist(), [s for _, s in w.groups()], 32, 8)
+
+
+def test_backward_needs_bf16_d128_and_an_uploaded_layout():
+    lib = _lib.load()
+    L = _build([5], [[3]], hq=4, hkv=1, d=64)
+    dummy = ctypes.c_void_p(16)
+    args = [dummy] * 10
+    assert lib.pg_attn_bwd(L.handle, *args, 1, ctypes.c_float(0.1), None) == -5   # not uploaded
+    assert lib.pg_attn_bwd(None, *args, 1, ctypes.c_float(0.1), None) == -1

@@ -181,15 +181,16 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-_STREAM = {"q": 1, "k": 2, "v": 3}
+_STREAM = {"q": 1, "k": 2, "v": 3, "do": 4}   # "do": upstream gradient of O (backward)
 
 
 def draw_tensor(w: Workload, which: str, chunk_tokens: int = 4096) -> np.ndarray:
-    """Draw Q, K or V of workload ``w`` as ``[T, H, d]``.
+    """Draw Q, K, V or the upstream gradient dO ("do", shaped like Q) of
+    workload ``w`` as ``[T, H, d]``.
 
     Returns float32 for fp32 workloads and uint16 bf16 bits for bf16 ones.
     """
-    heads = w.num_q_heads if which == "q" else w.num_kv_heads
+    heads = w.num_q_heads if which in ("q", "do") else w.num_kv_heads
     if w.index >= 0:
         rng = _rng(w.index, _STREAM[which], w.seed)
     else:
