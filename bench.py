@@ -117,6 +117,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-unpacked", action="store_true", help="skip the unpacked-layout baseline")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing pg_attn_bwd")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against a known byte count)")
@@ -140,7 +141,7 @@ def main(argv=None):
         return 0
     import shared_prefix_packed_amd as pg
     from shared_prefix_packed_amd.baseline import unpacked_workload
-    from workloads import draw_qkv, make_workload, sha256
+    from workloads import draw_qkv, draw_tensor, make_workload, sha256
 
     pg.load()   # fails loudly without the built library
     w = make_workload(args.workload)
@@ -237,6 +238,36 @@ def main(argv=None):
         Lu.close()
         del qu, ku, vu, ou, lu
 
+    # backward on the same batch: dQ, dK, dV for a seeded upstream gradient dO
+    bwd = None
+    if not args.no_backward and w.dtype == "bf16" and d == 128:
+        do = dev(draw_tensor(w, "do"))
+        L = build()
+        dq, dk, dv = torch.empty_like(qr), torch.empty_like(kr), torch.empty_like(v)
+        delta = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+        run_bwd = lambda: pg.pg_attn_bwd(L, qr, kr, v, o, lse, do, w.softmax_scale, dq=dq, dk=dk,
+                                         dv=dv, delta=delta, stream=stream)
+        for _ in range(2):
+            run_bwd()
+        ts = []
+        for _ in range(max(3, args.steps // 2)):
+            a_, b_ = ev(), ev()
+            a_.record(stream)
+            run_bwd()
+            b_.record(stream)
+            ts.append((a_, b_))
+        torch.cuda.synchronize()
+        bwd_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in ts]))
+        bwd_flop = 10 * d * Hq * int(summ.useful_pairs)
+        bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
+        bwd = {"ms": round(bwd_ms, 4), "useful_flop": bwd_flop,
+               "useful_tflops": round(bwd_tflops, 2),
+               "pct_of_bf16_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
+               "flop_definition": "10 * d * Hq per allowed (query, key) pair: S, dP, dV, dQ, dK products",
+               "kernels": "bwd_delta_kernel + bwd_dq_kernel + bwd_dkv_kernel, one pg_attn_bwd call"}
+        L.close()
+        del do, dq, dk, dv, delta
+
     traffic = load_traffic(w.name)
     roof = {
         "bound": "mfma",
@@ -290,6 +321,7 @@ def main(argv=None):
         "unpacked_attn_ms": None if unpacked_ms is None else round(unpacked_ms, 4),
         "speedup_vs_unpacked": None if speedup is None else round(speedup, 3),
         "roofline": roof,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
