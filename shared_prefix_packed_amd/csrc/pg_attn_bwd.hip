@@ -71,24 +71,32 @@ __device__ inline int rowmajor_off(int b, int lane, int row_bytes) {
   return row * row_bytes + 16 * chunk;
 }
 
-// Byte offset of the 16-byte global unit that lane `lane` of 1 KB block `b`
-// brings into a tile laid out for transposing reads: 512-byte read block
-// rb = 2 b + lane / 32 (index 8 ks + 4 rd + db) holds, at 16-byte unit u,
-// row 16 ks + 8 rd + 4 (u/16) + (u%8)/2 and d = 32 db + 16 ((u/8)&1) + 8 (u&1).
-__device__ inline int trread_off(int b, int lane, int row_bytes) {
-  const int rb = 2 * b + (lane >> 5);
-  const int ks = rb >> 3, rd = (rb >> 2) & 1, db = rb & 3;
-  const int u = lane & 31, g = u >> 3;
-  const int row = 16 * ks + 8 * rd + 4 * (g >> 1) + ((u & 7) >> 1);
-  const int d0 = 32 * db + 16 * (g & 1) + 8 * (u & 1);
-  return row * row_bytes + 2 * d0;
-}
+// Lane offsets of the transposing reads that take MFMA operand fragments out
+// of a row-major tile (256-byte rows, 16-byte chunks XOR-swizzled by row % 16):
+// within each 16-lane group the lanes address a 4-row x 32-byte block, lane
+// 4 j + c pointing at 4 columns 4c..4c+3 of row j, so that lane n receives
+// column n of the 4 rows. For the 16-row step s (rows 16 s + 4 (lane / 32) +
+// 0..3, then + 8: the accumulators' row order) and column block db the two
+// reads sit at tile + 4096 s + lo[db] and + hi[db]; row % 16 does not depend
+// on s, so neither does the swizzle.
+struct TrOffsets {
+  int lo[4], hi[4];
+  __device__ explicit TrOffsets(int lane) {
+    const int rlo = 4 * (lane >> 5) + ((lane >> 2) & 3);
+    const int rhi = rlo + 8;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int byte = 64 * db + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+      const int c16 = byte >> 4, within = byte & 15;
+      lo[db] = rlo * 256 + 16 * (c16 ^ (rlo & 15)) + within;
+      hi[db] = rhi * 256 + 16 * (c16 ^ (rhi & 15)) + within;
+    }
+  }
+};
 
-// The two transposing reads that form one MFMA operand fragment (8 bf16: rows
-// 16 ks .. 16 ks + 15 of column 32 db + lane % 32 in the accumulators' order).
-__device__ inline bf16x8_t tr_operand(const unsigned char* vb, int ks, int db) {
-  const i16x4_t lo = lds_read_tr(vb + 512 * (8 * ks + db));
-  const i16x4_t hi = lds_read_tr(vb + 512 * (8 * ks + 4 + db));
+__device__ inline bf16x8_t tr_rowmajor(const unsigned char* tile, const TrOffsets& o, int s, int db) {
+  const i16x4_t lo = lds_read_tr(tile + 4096 * s + o.lo[db]);
+  const i16x4_t hi = lds_read_tr(tile + 4096 * s + o.hi[db]);
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -184,9 +192,9 @@ constexpr int Q_KT = PG_KEY_TILE;            // 64 keys per tile
 constexpr int Q_QW = PG_WAVE_QUERIES;        // 32 query rows per wave
 constexpr int Q_WAVES = PG_ITEM_WAVES;       // 8 waves, as the forward's items
 constexpr int Q_REGION = Q_KT * D * 2;       // 16 KB
-constexpr int Q_STAGE = 3 * Q_REGION;        // K row-major, V row-major, K for transposing reads
-constexpr int Q_NSTAGE = 3;
-constexpr int Q_LOADS = 6;                   // 1 KB loads per wave per tile
+constexpr int Q_STAGE = 2 * Q_REGION;        // K, V row-major (K^T by transposing reads of K)
+constexpr int Q_NSTAGE = 4;
+constexpr int Q_LOADS = 4;                   // 1 KB loads per wave per tile
 
 struct BwdArgs {
   const uint16_t* q;
@@ -264,9 +272,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int s = it.span0; s < it.span0 + it.nspan; ++s)
     ntiles += (ld_scalar(a.spans, 2 * s + 1) - ld_scalar(a.spans, 2 * s) + Q_KT - 1) / Q_KT;
 
-  // staging: waves 0-3 bring K row-major (blocks 4 w + i) and the first half
-  // of K for transposing reads (blocks 2 w + i); waves 4-7 bring V row-major
-  // and the second half.
+  // staging: waves 0-3 bring K (blocks 4 w + i), waves 4-7 V
   const int w4 = wave & 3;
   const bool vgrp = wave >= 4;
   const int kv_row_bytes = a.Hkv * D * 2;
@@ -278,31 +284,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
     goff[i] = rowmajor_off(4 * w4 + i, lane, kv_row_bytes);
     ldst[i] = (vgrp ? Q_REGION : 0) + 1024 * (4 * w4 + i);
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int b = (vgrp ? 8 : 0) + 2 * w4 + i;
-    goff[4 + i] = trread_off(b, lane, kv_row_bytes);
-    ldst[4 + i] = 2 * Q_REGION + 1024 * b;
-  }
   auto fetch = [&](int ka, int k1, int stage) {
     ka = __builtin_amdgcn_readfirstlane(ka);
     k1 = __builtin_amdgcn_readfirstlane(k1);
     const int bytes = (k1 - ka - 1) * kv_row_bytes + D * 2;
     const int64_t row0 = (int64_t(ka) * a.Hkv + hk) * D;
-    const i32x4_t rk = make_rsrc(a.k + row0, bytes);
-    const i32x4_t rrm = vgrp ? make_rsrc(a.v + row0, bytes) : rk;
+    const i32x4_t rs = make_rsrc((vgrp ? a.v : a.k) + row0, bytes);
     const uint32_t sb = lds_base + uint32_t(stage * Q_STAGE);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buf16_to_lds(rrm, goff[i], sb + ldst[i]);
-#pragma unroll
-    for (int i = 4; i < Q_LOADS; ++i) buf16_to_lds(rk, goff[i], sb + ldst[i]);
+    for (int i = 0; i < Q_LOADS; ++i) buf16_to_lds(rs, goff[i], sb + ldst[i]);
   };
 
   // A operand reads: row-major K/V row 32 kb + qi, chunk 2 ks + half (swizzled)
   int koff[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * 256 + 16 * ((2 * ks + half) ^ (qi & 15));
-  const int troff = 2 * Q_REGION + 8 * lane;
+  const TrOffsets tro(lane);
 
   f32x16_t dqacc[4];
 #pragma unroll
@@ -312,24 +309,25 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
 
   SpanTiles ld, cp;
   ld.init(a.spans, it.span0, it.nspan);
-  fetch(ld.ka, ld.k1, 0);
-  ld.next(a.spans);
-  if (ntiles > 1) {
-    fetch(ld.ka, ld.k1, 1);
+  for (int n = 0; n < 3 && n < ntiles; ++n) {
+    fetch(ld.ka, ld.k1, n);
     ld.next(a.spans);
   }
   cp.init(a.spans, it.span0, it.nspan);
 
   for (int n = 0; n < ntiles; ++n) {
-    // tile n landed (tile n + 1 may still be in flight); after the barrier
-    // every wave is done with tile n - 1, whose stage tile n + 2 takes
-    if (n + 1 < ntiles)
+    // tile n landed (tiles n + 1, n + 2 may still be in flight); after the
+    // barrier every wave is done with tile n - 1, whose stage tile n + 3 takes
+    const int ahead = min(ntiles - 1 - n, 2);
+    if (ahead == 2)
+      wait_vmem<2 * Q_LOADS>();
+    else if (ahead == 1)
       wait_vmem<Q_LOADS>();
     else
       wait_vmem<0>();
     bare_barrier();
-    if (n + 2 < ntiles) {
-      fetch(ld.ka, ld.k1, (n + 2) % Q_NSTAGE);
+    if (n + 3 < ntiles) {
+      fetch(ld.ka, ld.k1, (n + 3) % Q_NSTAGE);
       ld.next(a.spans);
     }
     const int ka = cp.ka, k1 = cp.k1;
@@ -384,13 +382,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) dsf[ks] = pack_step(sacc[ks >> 1], ks);
 
-    // dQ^T += K^T dS^T
-    const unsigned char* vb = st + troff;
+    // dQ^T += K^T dS^T (K^T by transposing reads of the row-major K tile)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(vb, ks, db), dsf[ks],
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rowmajor(st, tro, ks, db), dsf[ks],
                                                             dqacc[db], 0, 0, 0);
     sched_reads_ahead<6, 2, 16>();
   }
@@ -405,10 +402,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dK, dV --
 
-constexpr int KV_QT = 32;                    // query rows per tile
+constexpr int KV_QT = 64;                    // query rows per tile
 constexpr int KV_WAVES = 4;                  // 32 keys each (PG_KV_BLOCK = 128)
-constexpr int KV_REGION = KV_QT * D * 2;     // 8 KB
-constexpr int KV_ROWS = 4 * KV_REGION;       // Q, dO row-major; Q, dO for transposing reads
+constexpr int KV_REGION = KV_QT * D * 2;     // 16 KB
+constexpr int KV_ROWS = 2 * KV_REGION;       // Q, dO row-major
 constexpr int KV_STAGE = KV_ROWS + 3 * 256;  // + lse, D, and a sink for unused lanes' loads
 constexpr int KV_NSTAGE = 3;
 constexpr int KV_LOADS = 9;                  // per wave per tile: 8 x 1 KB + one 256 B load
@@ -456,30 +453,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
       dvacc[db][i] = 0.f;
     }
 
-  // query tiles: rows q0 = k0 + 32 m (m < nq) for each query head of hk
+  // query tiles: rows q0 = k0 + 64 m (m < nq) for each query head of hk
   const int q_start = it.k0;
   const int nq = (it.qend - q_start + KV_QT - 1) / KV_QT;
   const int ntiles = nq * a.r;
   const int q_row_bytes = a.Hq * D * 2;
 
-  // staging: wave w brings blocks 2 w, 2 w + 1 of each 8 KB region
-  // (Q, dO row-major; Q, dO for transposing reads) and one 256 B row:
-  // wave 0 lse, wave 1 D, waves 2-3 an empty load into the sink
+  // staging: wave w brings blocks 4 w .. 4 w + 3 of the row-major Q and dO
+  // tiles and one 256 B row: wave 0 the rows' lse, wave 1 their D, waves 2-3
+  // an empty load into the sink
   const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
-  int goff[8];
-  uint32_t ldst[8];
+  int goff[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int b = 2 * wave + i;
-    goff[0 + i] = rowmajor_off(b, lane, q_row_bytes);           // Q row-major
-    ldst[0 + i] = 0 * KV_REGION + 1024 * b;
-    goff[2 + i] = goff[0 + i];                                  // dO row-major
-    ldst[2 + i] = 1 * KV_REGION + 1024 * b;
-    goff[4 + i] = trread_off(b, lane, q_row_bytes);             // Q transposing
-    ldst[4 + i] = 2 * KV_REGION + 1024 * b;
-    goff[6 + i] = goff[4 + i];                                  // dO transposing
-    ldst[6 + i] = 3 * KV_REGION + 1024 * b;
-  }
+  for (int i = 0; i < 4; ++i) goff[i] = rowmajor_off(4 * wave + i, lane, q_row_bytes);
   auto fetch = [&](int n, int stage) {
     const int m = n / a.r, h = hk * a.r + n % a.r;
     const int q0 = q_start + KV_QT * m;
@@ -488,26 +474,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int64_t row0 = (int64_t(q0) * a.Hq + h) * D;
     const i32x4_t rq = make_rsrc(a.q + row0, bytes);
     const i32x4_t rd = make_rsrc(a.dout + row0, bytes);
-    const uint32_t sb = lds_base + uint32_t(stage * KV_STAGE);
-    buf16_to_lds(rq, goff[0], sb + ldst[0]);
-    buf16_to_lds(rq, goff[1], sb + ldst[1]);
-    buf16_to_lds(rd, goff[2], sb + ldst[2]);
-    buf16_to_lds(rd, goff[3], sb + ldst[3]);
-    buf16_to_lds(rq, goff[4], sb + ldst[4]);
-    buf16_to_lds(rq, goff[5], sb + ldst[5]);
-    buf16_to_lds(rd, goff[6], sb + ldst[6]);
-    buf16_to_lds(rd, goff[7], sb + ldst[7]);
-    // the tile's 32 lse (wave 0) or D (wave 1) values; lanes past the rows
+    const uint32_t sb = lds_base + uint32_t(stage * KV_STAGE) + 4096 * wave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf16_to_lds(rq, goff[i], sb + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf16_to_lds(rd, goff[i], sb + KV_REGION + 1024 * i);
+    // the tile's 64 lse (wave 0) or D (wave 1) values; lanes past the rows
     // read zeros
     const float* src = wave == 0 ? a.lse : a.delta;
     const i32x4_t rl = make_rsrc(src + int64_t(h) * a.T + q0, wave < 2 ? 4 * rows : 0);
-    buf4_to_lds(rl, 4 * lane, sb + KV_ROWS + 256 * min(wave, 2));
+    buf4_to_lds(rl, 4 * lane, lds_base + uint32_t(stage * KV_STAGE) + KV_ROWS + 256 * min(wave, 2));
   };
 
-  // A operand reads of row-major Q / dO: row col, chunk 2 ks + half (swizzled)
+  // A operand reads of row-major Q / dO: row 32 kb + col, chunk 2 ks + half
   int aoff[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) aoff[ks] = col * 256 + 16 * ((2 * ks + half) ^ (col & 15));
+  const TrOffsets tro(lane);
 
   fetch(0, 0);
   if (ntiles > 1) fetch(1, 1);
@@ -525,62 +508,68 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     if (q0 + KV_QT - 1 < kw0) continue;
     const unsigned char* st = smem + (n % KV_NSTAGE) * KV_STAGE;
 
-    f32x16_t sacc, pacc;
+    f32x16_t sacc[2], pacc[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sacc[i] = 0.f;
-      pacc[i] = 0.f;
+      sacc[0][i] = 0.f;
+      sacc[1][i] = 0.f;
+      pacc[0][i] = 0.f;
+      pacc[1][i] = 0.f;
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t aq = as_bf16x8(*reinterpret_cast<const uint4*>(st + aoff[ks]));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t ad = as_bf16x8(*reinterpret_cast<const uint4*>(st + KV_REGION + aoff[ks]));
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], pacc, 0, 0, 0);
-    }
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t aq = as_bf16x8(*reinterpret_cast<const uint4*>(st + 8192 * kb + aoff[ks]));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc[kb], 0, 0, 0);
+      }
+    sched_reads_ahead<4, 1, 16>();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t ad =
+            as_bf16x8(*reinterpret_cast<const uint4*>(st + KV_REGION + 8192 * kb + aoff[ks]));
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], pacc[kb], 0, 0, 0);
+      }
     sched_reads_ahead<4, 1, 16>();
 
-    // register i holds query row q0 + 8 (i/4) + 4 half + i%4 of key `key`
+    // register i of block kb holds query row q0 + 32 kb + 8 (i/4) + 4 half + i%4
     const float* lse_t = reinterpret_cast<const float*>(st + KV_ROWS);
     const float* dlt_t = reinterpret_cast<const float*>(st + KV_ROWS + 256);
     const bool full = (q0 >= kw0 + 31) && (q0 + KV_QT <= it.qend);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r0 = 8 * g + 4 * half;
-      const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
-      const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + r0);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g + j;
-        const int qrow = q0 + r0 + j;
-        float p = fast_exp2(fmaf(sacc[i], a.c_log2, -(&l4.x)[j] * LOG2E));
-        if (!full) p = (qrow >= key && qrow < it.qend) ? p : 0.f;
-        pacc[i] = p * (pacc[i] - (&d4.x)[j]);   // dS
-        sacc[i] = p;                            // P
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = 32 * kb + 8 * g + 4 * half;
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
+        const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + r0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * g + j;
+          const int qrow = q0 + r0 + j;
+          float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -(&l4.x)[j] * LOG2E));
+          if (!full) p = (qrow >= key && qrow < it.qend) ? p : 0.f;
+          pacc[kb][i] = p * (pacc[kb][i] - (&d4.x)[j]);   // dS
+          sacc[kb][i] = p;                                // P
+        }
       }
-    }
-    bf16x8_t pf[2], dsf[2];
+    // dV += P^T dO, dK += dS^T Q (B by transposing reads of the row-major
+    // dO and Q tiles)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      pf[s] = pack_step(sacc, s);
-      dsf[s] = pack_step(pacc, s);
-    }
-    // dV += P^T dO, dK += dS^T Q (B by transposing reads of dO, Q)
-    const unsigned char* vq = st + 2 * KV_REGION + 8 * lane;
-    const unsigned char* vd = st + 3 * KV_REGION + 8 * lane;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const bf16x8_t pf = pack_step(sacc[s2 >> 1], s2);
+      const bf16x8_t dsf = pack_step(pacc[s2 >> 1], s2);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[s], tr_operand(vd, s, db),
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, tr_rowmajor(st + KV_REGION, tro, s2, db),
                                                             dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[s], tr_operand(vq, s, db),
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf, tr_rowmajor(st, tro, s2, db),
                                                             dkacc[db], 0, 0, 0);
       }
-    sched_reads_ahead<8, 2, 16>();
+    }
+    sched_reads_ahead<8, 2, 32>();
   }
 
   wait_vmem<0>();
