@@ -487,6 +487,67 @@ def backward_flop(lay, head_dim: int, num_q_heads: int) -> int:
     return 10 * head_dim * num_q_heads * useful_pairs(lay)
 
 
+# -------------------------------------------------------- pack and unpack --
+
+
+def pack_rows(prefix: np.ndarray, suffix: np.ndarray, lay) -> np.ndarray:
+    """Packed rows from right-padded per-group prompts and per-response rows.
+
+    verl page, section 2 (building the grouped batch: the prompts selected once
+    per group are concatenated with the responses, right padding): the packed
+    row of group g is prompt_g followed by each of its responses, groups one
+    after another. prefix: [G, Pmax, ...] (first prefix_lens[g] rows valid),
+    suffix: [N, Smax, ...] (first suffix_lens[k] rows valid, responses in group
+    order). Returns [T, ...], written out by concatenation.
+    Pinned by: a hand-written example; unpack_rows(pack_rows(x)) gives the
+    valid rows back.
+    """
+    parts = []
+    k = 0
+    for g in range(len(lay["prefix_lens"])):
+        parts.append(prefix[g, :int(lay["prefix_lens"][g])])
+        for _ in range(int(lay["suffix_counts"][g])):
+            parts.append(suffix[k, :int(lay["suffix_lens"][k])])
+            k += 1
+    if not parts:
+        return np.zeros((0,) + prefix.shape[2:], dtype=prefix.dtype)
+    return np.concatenate(parts, axis=0)
+
+
+def unpack_rows(packed: np.ndarray, lay, prefix_pad: int, suffix_pad: int):
+    """Split packed rows back per group and per response, the last prompt row
+    included in each response part.
+
+    verl page, section 3 (forward: the output is split into prefix and suffix
+    parts with the last prefix position included; the caller drops the last
+    column): prefix_out[g, i] = packed row of prompt token i of group g;
+    suffix_out[k, 0] = the group's last prompt row (its logit predicts the
+    response's first token), suffix_out[k, 1 + j] = row of response token j.
+    Reading where the pages are silent: padding rows are zero, and a group
+    without a prompt gives a zero first row. Returns (prefix_out [G,
+    prefix_pad, ...], suffix_out [N, suffix_pad + 1, ...]).
+    """
+    G = len(lay["prefix_lens"])
+    N = len(lay["suffix_lens"])
+    tail = packed.shape[1:]
+    pre = np.zeros((G, prefix_pad) + tail, dtype=packed.dtype)
+    suf = np.zeros((N, suffix_pad + 1) + tail, dtype=packed.dtype)
+    k = 0
+    for g in range(G):
+        a = int(lay["group_off"][g])
+        P = int(lay["prefix_lens"][g])
+        pre[g, :P] = packed[a:a + P]
+        cur = a + P
+        for _ in range(int(lay["suffix_counts"][g])):
+            S = int(lay["suffix_lens"][k])
+            if P > 0:
+                suf[k, 0] = packed[a + P - 1]
+            suf[k, 1:1 + S] = packed[cur:cur + S]
+            cur += S
+            k += 1
+    return pre, suf
+
+
 # ---------------------------------------------------------- FLOP accounting --
 
 
