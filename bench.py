@@ -118,6 +118,7 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-unpacked", action="store_true", help="skip the unpacked-layout baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip timing pg_attn_bwd")
+    ap.add_argument("--no-gathers", action="store_true", help="skip timing pg_pack_rows / pg_unpack_rows")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against a known byte count)")
@@ -268,6 +269,42 @@ def main(argv=None):
         L.close()
         del do, dq, dk, dv, delta
 
+    # pack / unpack gathers either side of the path, on hidden-state rows
+    gathers = None
+    if not args.no_gathers:
+        hidden = 2048
+        Gn, Nn = len(w.prefix_lens), len(w.suffix_lens)
+        ppad, spad = int(w.prefix_lens.max()), int(w.suffix_lens.max())
+        L = build()
+        pre = torch.randn((Gn, ppad, hidden), device="cuda").to(torch.bfloat16)
+        suf = torch.randn((Nn, spad, hidden), device="cuda").to(torch.bfloat16)
+        packed = torch.empty((T, hidden), dtype=torch.bfloat16, device="cuda")
+        for _ in range(2):
+            pg.pg_pack_rows(L, pre, suf, packed=packed, stream=stream)
+            pg.pg_unpack_rows(L, packed, ppad, spad, stream=stream)
+        tp, tu = [], []
+        for _ in range(max(3, args.steps // 2)):
+            a_, b_, c_ = ev(), ev(), ev()
+            a_.record(stream)
+            pg.pg_pack_rows(L, pre, suf, packed=packed, stream=stream)
+            b_.record(stream)
+            outs = pg.pg_unpack_rows(L, packed, ppad, spad, stream=stream)
+            c_.record(stream)
+            tp.append((a_, b_))
+            tu.append((b_, c_))
+        torch.cuda.synchronize()
+        pms = float(np.mean([x.elapsed_time(y) for x, y in tp]))
+        ums = float(np.mean([x.elapsed_time(y) for x, y in tu]))
+        rb = hidden * 2
+        pack_bytes = 2 * T * rb                                         # read + write each packed row
+        unpack_bytes = (T + Nn) * rb + (Gn * ppad + Nn * (spad + 1)) * rb   # rows read, padded outputs written
+        gathers = {"row_bytes": rb,
+                   "pack_ms": round(pms, 4), "pack_gbs": round(pack_bytes / (pms * 1e-3) / 1e9, 1),
+                   "unpack_ms": round(ums, 4), "unpack_gbs": round(unpack_bytes / (ums * 1e-3) / 1e9, 1),
+                   "hbm_peak_gbs": PEAK_HBM_GBS}
+        L.close()
+        del pre, suf, packed, outs
+
     traffic = load_traffic(w.name)
     roof = {
         "bound": "mfma",
@@ -322,6 +359,7 @@ def main(argv=None):
         "speedup_vs_unpacked": None if speedup is None else round(speedup, 3),
         "roofline": roof,
         "backward": bwd,
+        "gathers": gathers,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -236,6 +236,39 @@ pg_status pg_attn_fwd(const pg_layout* layout, const void* q, const void* k, con
                       hipStream_t stream);
 
 /*
+ * pg_pack_rows -- build packed rows from right-padded per-prompt and
+ * per-response rows: packed row t is row t - g0 of its group's prompt or row
+ * t - (response start) of its response (verl prefix_grouper_utils.py page,
+ * section 2: each prompt once, then its responses, right padding).
+ *  prefix  [G, prefix_pad] rows (first prefix_lens[g] of group g used)
+ *  suffix  [N, suffix_pad] rows, responses in group order (first suffix_lens[k] used)
+ *  packed  [T] rows, written completely
+ *  row_bytes  size of one row, a positive multiple of 4 (ids, hidden states,
+ *             logits: any row type)
+ * prefix_pad / suffix_pad must cover the longest prompt / response. Device
+ * pointers; PG_ERR_INVALID_ARG on bad sizes or NULL where rows are needed.
+ */
+pg_status pg_pack_rows(const pg_layout* layout, const void* prefix, int32_t prefix_pad,
+                       const void* suffix, int32_t suffix_pad, void* packed, int64_t row_bytes,
+                       hipStream_t stream);
+
+/*
+ * pg_unpack_rows -- split packed rows back per prompt and per response, the
+ * response part led by its group's last prompt row (verl page, section 3: the
+ * output is split with the last prefix position included, whose logit
+ * predicts the response's first token).
+ *  prefix_out [G, prefix_pad] rows or NULL: row i of group g = packed row of
+ *             prompt token i; zero past the prompt
+ *  suffix_out [N, suffix_pad + 1] rows or NULL: row 0 = the group's last prompt
+ *             row (zero for a group without prompt), row 1 + j = response
+ *             token j; zero past the response
+ * Both outputs are written completely. row_bytes as for pg_pack_rows.
+ */
+pg_status pg_unpack_rows(const pg_layout* layout, const void* packed, int64_t row_bytes,
+                         void* prefix_out, int32_t prefix_pad, void* suffix_out,
+                         int32_t suffix_pad, hipStream_t stream);
+
+/*
  * pg_attn_bwd -- gradients of pg_attn_fwd's output O for an upstream gradient
  * dO: dQ, dK, dV. The derivative of the packed attention, by the chain rule:
  * with P the softmax of a row over its key set, dV = P^T dO, dS = P (dO V^T -

@@ -11,7 +11,9 @@ from .api import (  # noqa: F401
     pg_build_layout,
     pg_build_layout_host,
     pg_layout_upload,
+    pg_pack_rows,
     pg_position_ids,
     pg_rope,
+    pg_unpack_rows,
 )
 from ._lib import PgError, load  # noqa: F401

@@ -76,6 +76,10 @@ SIGNATURES = {
     "pg_attn_bwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                               ctypes.c_float, c_void_p]),
+    "pg_pack_rows": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                               ctypes.c_int64, c_void_p]),
+    "pg_unpack_rows": (c_int32, [c_void_p, c_void_p, ctypes.c_int64, c_void_p, c_int32,
+                                 c_void_p, c_int32, c_void_p]),
     "pg_status_string": (ctypes.c_char_p, [c_int32]),
     "pg_last_error": (ctypes.c_char_p, []),
 }

@@ -248,3 +248,49 @@ def pg_attn_bwd(layout: Layout, q, k, v, o, lse, dout, softmax_scale: float, dq=
                              float(softmax_scale), _stream_handle(stream)),
           "pg_attn_bwd")
     return dq, dk, dv
+
+
+def _row_bytes(t, lead: int) -> int:
+    n = 1
+    for x in t.shape[lead:]:
+        n *= int(x)
+    return n * t.element_size()
+
+
+def pg_pack_rows(layout: Layout, prefix, suffix, packed=None, stream=None):
+    """Packed rows [T, ...] from right-padded prompts [G, Ppad, ...] and
+    responses [N, Spad, ...] (any dtype; rows of a multiple of 4 bytes)."""
+    import torch
+    if not (prefix.is_contiguous() and suffix.is_contiguous()):
+        raise ValueError("prefix and suffix must be contiguous")
+    if prefix.dtype != suffix.dtype or prefix.shape[2:] != suffix.shape[2:]:
+        raise ValueError("prefix and suffix rows differ")
+    T = layout.total_tokens
+    if packed is None:
+        packed = torch.empty((T,) + tuple(prefix.shape[2:]), dtype=prefix.dtype, device=prefix.device)
+    check(load().pg_pack_rows(layout.handle, ctypes.c_void_p(prefix.data_ptr()), int(prefix.shape[1]),
+                              ctypes.c_void_p(suffix.data_ptr()), int(suffix.shape[1]),
+                              ctypes.c_void_p(packed.data_ptr()), _row_bytes(prefix, 2),
+                              _stream_handle(stream)),
+          "pg_pack_rows")
+    return packed
+
+
+def pg_unpack_rows(layout: Layout, packed, prefix_pad: int, suffix_pad: int, stream=None):
+    """(prefix_out [G, prefix_pad, ...], suffix_out [N, suffix_pad + 1, ...]):
+    the packed rows split back, each response part led by its group's last
+    prompt row."""
+    import torch
+    if not packed.is_contiguous():
+        raise ValueError("packed must be contiguous")
+    s = layout.summary()
+    n_resp = int(np.asarray(layout.offsets()[1]).size - 1 - s.num_groups)
+    tail = tuple(packed.shape[1:])
+    pre = torch.empty((s.num_groups, prefix_pad) + tail, dtype=packed.dtype, device=packed.device)
+    suf = torch.empty((n_resp, suffix_pad + 1) + tail, dtype=packed.dtype, device=packed.device)
+    check(load().pg_unpack_rows(layout.handle, ctypes.c_void_p(packed.data_ptr()),
+                                _row_bytes(packed, 1), ctypes.c_void_p(pre.data_ptr()),
+                                int(prefix_pad), ctypes.c_void_p(suf.data_ptr()), int(suffix_pad),
+                                _stream_handle(stream)),
+          "pg_unpack_rows")
+    return pre, suf

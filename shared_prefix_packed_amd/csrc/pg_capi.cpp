@@ -101,7 +101,14 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   const size_t off_sp = align_up(off_it + sizeof(pg_work_item) * L->items.size(), A);
   const size_t off_fr = align_up(off_sp + sizeof(pg_key_span) * L->spans.size(), A);
   const size_t off_kv = align_up(off_fr + sizeof(double) * L->inv_freq.size(), A);
-  const size_t bytes = align_up(off_kv + sizeof(pg_kv_item) * L->kv_items.size(), A);
+  const size_t G = L->group_off.size() - 1, N = L->suffix_lens.size();
+  const size_t off_ow = align_up(off_kv + sizeof(pg_kv_item) * L->kv_items.size(), A);
+  const size_t off_go = align_up(off_ow + 4 * T, A);
+  const size_t off_pl = align_up(off_go + 4 * (G + 1), A);
+  const size_t off_so = align_up(off_pl + 4 * G, A);
+  const size_t off_sg = align_up(off_so + 4 * L->seg_off.size(), A);
+  const size_t off_sl = align_up(off_sg + 4 * N, A);
+  const size_t bytes = align_up(off_sl + 4 * N, A);
   hipError_t e = hipGetDevice(&L->device);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   pg_slot* slot = nullptr;
@@ -118,6 +125,14 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   std::memcpy(h + off_fr, L->inv_freq.data(), sizeof(double) * L->inv_freq.size());
   if (!L->kv_items.empty())
     std::memcpy(h + off_kv, L->kv_items.data(), sizeof(pg_kv_item) * L->kv_items.size());
+  std::memcpy(h + off_ow, L->tok_owner.data(), 4 * T);
+  std::memcpy(h + off_go, L->group_off.data(), 4 * (G + 1));
+  if (G) std::memcpy(h + off_pl, L->prefix_lens.data(), 4 * G);
+  std::memcpy(h + off_so, L->seg_off.data(), 4 * L->seg_off.size());
+  if (N) {
+    std::memcpy(h + off_sg, L->suffix_group.data(), 4 * N);
+    std::memcpy(h + off_sl, L->suffix_lens.data(), 4 * N);
+  }
   void* d = slot->dev;
   e = hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) {
@@ -135,6 +150,12 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   L->d_spans = reinterpret_cast<const pg_key_span*>(b + off_sp);
   L->d_inv_freq = reinterpret_cast<const double*>(b + off_fr);
   L->d_kv_items = reinterpret_cast<const pg_kv_item*>(b + off_kv);
+  L->d_owner = reinterpret_cast<const int32_t*>(b + off_ow);
+  L->d_group_off = reinterpret_cast<const int32_t*>(b + off_go);
+  L->d_prefix_lens = reinterpret_cast<const int32_t*>(b + off_pl);
+  L->d_seg_off = reinterpret_cast<const int32_t*>(b + off_so);
+  L->d_suffix_group = reinterpret_cast<const int32_t*>(b + off_sg);
+  L->d_suffix_lens = reinterpret_cast<const int32_t*>(b + off_sl);
   return PG_OK;
 }
 
@@ -275,6 +296,45 @@ pg_status pg_attn_bwd(const pg_layout* L, const void* q, const void* k, const vo
                                     stream);
   pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "backward kernel launch");
+}
+
+pg_status pg_pack_rows(const pg_layout* L, const void* prefix, int32_t prefix_pad,
+                       const void* suffix, int32_t suffix_pad, void* packed, int64_t row_bytes,
+                       hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (row_bytes <= 0 || row_bytes % 4 != 0)
+    return pg_fail(PG_ERR_INVALID_ARG, "row_bytes %lld must be a positive multiple of 4",
+                   (long long)row_bytes);
+  if (prefix_pad < L->max_prefix_len || suffix_pad < L->max_suffix_len)
+    return pg_fail(PG_ERR_INVALID_ARG, "padding (%d, %d) shorter than the longest prompt %d / response %d",
+                   prefix_pad, suffix_pad, L->max_prefix_len, L->max_suffix_len);
+  if (L->T == 0) return PG_OK;
+  if (!packed || (L->max_prefix_len > 0 && !prefix) || (L->max_suffix_len > 0 && !suffix))
+    return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e = pg_launch_pack(*L, prefix, prefix_pad, suffix, suffix_pad, packed, row_bytes, stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "pack kernel launch");
+}
+
+pg_status pg_unpack_rows(const pg_layout* L, const void* packed, int64_t row_bytes,
+                         void* prefix_out, int32_t prefix_pad, void* suffix_out, int32_t suffix_pad,
+                         hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (row_bytes <= 0 || row_bytes % 4 != 0)
+    return pg_fail(PG_ERR_INVALID_ARG, "row_bytes %lld must be a positive multiple of 4",
+                   (long long)row_bytes);
+  if ((prefix_out && prefix_pad < L->max_prefix_len) || (suffix_out && suffix_pad < L->max_suffix_len))
+    return pg_fail(PG_ERR_INVALID_ARG, "padding (%d, %d) shorter than the longest prompt %d / response %d",
+                   prefix_pad, suffix_pad, L->max_prefix_len, L->max_suffix_len);
+  if (prefix_pad < 0 || suffix_pad < 0) return pg_fail(PG_ERR_INVALID_ARG, "negative padding");
+  if ((prefix_out || suffix_out) && L->T > 0 && !packed)
+    return pg_fail(PG_ERR_INVALID_ARG, "packed is NULL");
+  hipError_t e = pg_launch_unpack(*L, packed, row_bytes, prefix_out, prefix_pad, suffix_out,
+                                  suffix_pad, stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "unpack kernel launch");
 }
 
 }  // extern "C"

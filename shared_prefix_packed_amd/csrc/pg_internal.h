@@ -45,6 +45,9 @@ struct pg_layout {
   std::vector<int32_t> group_off;   // [G+1]
   std::vector<int32_t> seg_off;     // [num_segments+1]
   std::vector<int32_t> tok_g0, tok_pe, tok_ss;   // [T]
+  std::vector<int32_t> tok_owner;      // [T] group of a prompt token, response index of a response token
+  std::vector<int32_t> suffix_group;   // [N] group of each response
+  int32_t max_prefix_len = 0, max_suffix_len = 0;
   std::vector<double> inv_freq;     // [d/2], theta^(-2i/d)
   int32_t max_position = -1;
   int64_t useful_pairs = 0, unpacked_pairs = 0;
@@ -68,6 +71,12 @@ struct pg_layout {
   const pg_key_span* d_spans = nullptr;
   const double* d_inv_freq = nullptr;
   const pg_kv_item* d_kv_items = nullptr;
+  const int32_t* d_owner = nullptr;          // [T]
+  const int32_t* d_group_off = nullptr;      // [G+1]
+  const int32_t* d_prefix_lens = nullptr;    // [G]
+  const int32_t* d_seg_off = nullptr;        // [G+N+1]
+  const int32_t* d_suffix_group = nullptr;   // [N]
+  const int32_t* d_suffix_lens = nullptr;    // [N]
 };
 
 // Host layout builder (pg_layout.cpp). Validates and fills `L`.
@@ -89,6 +98,12 @@ hipError_t pg_launch_rope(const pg_layout& L, const int64_t* pos, const void* q_
 hipError_t pg_launch_attn_rowwise(const pg_layout& L, const void* q, const void* k,
                                   const void* v, void* o, float* lse, pg_dtype dtype,
                                   float softmax_scale, hipStream_t stream);
+hipError_t pg_launch_pack(const pg_layout& L, const void* prefix, int32_t prefix_pad,
+                          const void* suffix, int32_t suffix_pad, void* packed, int64_t row_bytes,
+                          hipStream_t stream);
+hipError_t pg_launch_unpack(const pg_layout& L, const void* packed, int64_t row_bytes,
+                            void* prefix_out, int32_t prefix_pad, void* suffix_out,
+                            int32_t suffix_pad, hipStream_t stream);
 hipError_t pg_launch_attn_bwd(const pg_layout& L, const void* q, const void* k, const void* v,
                               const void* o, const float* lse, const void* dout, void* dq,
                               void* dk, void* dv, float* delta, float softmax_scale,

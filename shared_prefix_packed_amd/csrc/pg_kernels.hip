@@ -207,6 +207,81 @@ __global__ __launch_bounds__(64) void attn_rowwise_kernel(
   if (lse && lane == 0) lse[int64_t(h) * Ttok + t] = (m + log2f(l)) * 0.69314718055994530942f;
 }
 
+
+// ------------------------------------------------------- pack and unpack --
+// Row gathers either side of the packed path (verl prefix_grouper_utils.py
+// page, sections 2-3: concatenating each prompt once with its responses, and
+// splitting the output back with the last prompt position included in each
+// response part). A row is `upr` units of U (16 bytes when the row size
+// allows, else 4); consecutive threads move consecutive units of a row.
+
+// packed[t] = prompt row (owner g, index t - g0) or response row (owner k,
+// index t - ss).
+template <typename U>
+__global__ __launch_bounds__(256) void pack_rows_kernel(const int32_t* __restrict__ owner,
+                                                        const int32_t* __restrict__ g0,
+                                                        const int32_t* __restrict__ pe,
+                                                        const int32_t* __restrict__ ss,
+                                                        const U* prefix, int64_t ppad,
+                                                        const U* suffix, int64_t spad, U* packed,
+                                                        int64_t rows, int64_t upr) {
+  const int64_t total = rows * upr;
+  for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = u / upr, c = u - t * upr;
+    const int32_t o = owner[t];
+    const U* src = t < pe[t] ? prefix + (o * ppad + (t - g0[t])) * upr
+                             : suffix + (o * spad + (t - ss[t])) * upr;
+    packed[u] = src[c];
+  }
+}
+
+// Output rows: prompt part [G, ppad] (row i of group g: packed row
+// group_off[g] + i if i < prefix_lens[g]), response part [N, spad + 1] (row 0:
+// the group's last prompt row; row 1 + j: response row j); zeros elsewhere and
+// everywhere when the layout has no tokens (no tables).
+template <typename U>
+__global__ __launch_bounds__(256) void unpack_rows_kernel(
+    const int32_t* __restrict__ group_off, const int32_t* __restrict__ prefix_lens,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ suffix_group,
+    const int32_t* __restrict__ suffix_lens, const U* packed, U* prefix_out, int64_t G,
+    int64_t ppad, U* suffix_out, int64_t N, int64_t spad, int64_t upr) {
+  const int64_t pre_rows = prefix_out ? G * ppad : 0;
+  const int64_t suf_rows = suffix_out ? N * (spad + 1) : 0;
+  const int64_t total = (pre_rows + suf_rows) * upr;
+  const bool have = group_off != nullptr;
+  for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t row = u / upr, c = u - row * upr;
+    int64_t src = -1;
+    U* dst;
+    if (row < pre_rows) {
+      const int64_t g = row / ppad, i = row - g * ppad;
+      if (have && i < prefix_lens[g]) src = group_off[g] + i;
+      dst = prefix_out + row * upr;
+    } else {
+      const int64_t r = row - pre_rows;
+      const int64_t k = r / (spad + 1), j = r - k * (spad + 1);
+      if (have) {
+        const int32_t g = suffix_group[k];
+        if (j == 0) {
+          if (prefix_lens[g] > 0) src = group_off[g] + prefix_lens[g] - 1;
+        } else if (j - 1 < suffix_lens[k]) {
+          src = seg_off[g + k + 1] + (j - 1);   // response k is segment g + k + 1
+        }
+      }
+      dst = suffix_out + r * upr;
+    }
+    U val;
+    if (src >= 0) {
+      val = packed[src * upr + c];
+    } else {
+      __builtin_memset(&val, 0, sizeof(U));
+    }
+    dst[c] = val;
+  }
+}
+
 }  // namespace
 
 hipError_t pg_launch_positions(const pg_layout& L, int64_t* pos, hipStream_t stream) {
@@ -250,5 +325,48 @@ hipError_t pg_launch_attn_rowwise(const pg_layout& L, const void* q, const void*
     if (L.d == 128) PG_ROW(float, 128); else PG_ROW(float, 64);
   }
 #undef PG_ROW
+  return hipGetLastError();
+}
+
+namespace {
+// grid for a grid-stride loop over `units` threads' worth of work
+dim3 gather_grid(int64_t units) {
+  const int64_t blocks = (units + 255) / 256;
+  return dim3(uint32_t(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536));
+}
+}  // namespace
+
+hipError_t pg_launch_pack(const pg_layout& L, const void* prefix, int32_t prefix_pad,
+                          const void* suffix, int32_t suffix_pad, void* packed, int64_t row_bytes,
+                          hipStream_t stream) {
+  if (L.T == 0) return hipSuccess;
+  if (row_bytes % 16 == 0) {
+    const int64_t upr = row_bytes / 16;
+    pack_rows_kernel<uint4><<<gather_grid(L.T * upr), dim3(256), 0, stream>>>(
+        L.d_owner, L.d_g0, L.d_pe, L.d_ss, static_cast<const uint4*>(prefix), prefix_pad,
+        static_cast<const uint4*>(suffix), suffix_pad, static_cast<uint4*>(packed), L.T, upr);
+  } else {
+    const int64_t upr = row_bytes / 4;
+    pack_rows_kernel<uint32_t><<<gather_grid(L.T * upr), dim3(256), 0, stream>>>(
+        L.d_owner, L.d_g0, L.d_pe, L.d_ss, static_cast<const uint32_t*>(prefix), prefix_pad,
+        static_cast<const uint32_t*>(suffix), suffix_pad, static_cast<uint32_t*>(packed), L.T,
+        upr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_unpack(const pg_layout& L, const void* packed, int64_t row_bytes,
+                            void* prefix_out, int32_t prefix_pad, void* suffix_out,
+                            int32_t suffix_pad, hipStream_t stream) {
+  const int64_t G = int64_t(L.group_off.size()) - 1, N = int64_t(L.suffix_lens.size());
+  const int64_t rows = (prefix_out ? G * prefix_pad : 0) + (suffix_out ? N * (suffix_pad + 1) : 0);
+  if (rows == 0) return hipSuccess;
+  const bool have = L.T > 0;   // a layout without tokens has no device tables: all zeros
+#define PG_UNPACK(U, W)                                                                            unpack_rows_kernel<U><<<gather_grid(rows * (row_bytes / W)), dim3(256), 0, stream>>>(              have ? L.d_group_off : nullptr, L.d_prefix_lens, L.d_seg_off, L.d_suffix_group,                L.d_suffix_lens, static_cast<const U*>(packed), static_cast<U*>(prefix_out), G,                 prefix_pad, static_cast<U*>(suffix_out), N, suffix_pad, row_bytes / W)
+  if (row_bytes % 16 == 0)
+    PG_UNPACK(uint4, 16);
+  else
+    PG_UNPACK(uint32_t, 4);
+#undef PG_UNPACK
   return hipGetLastError();
 }

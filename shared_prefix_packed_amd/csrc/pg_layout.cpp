@@ -141,6 +141,10 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
     L.tok_g0.resize(size_t(total));
     L.tok_pe.resize(size_t(total));
     L.tok_ss.resize(size_t(total));
+    L.tok_owner.resize(size_t(total));
+    L.suffix_group.assign(size_t(nsuf), 0);
+    L.max_prefix_len = 0;
+    L.max_suffix_len = 0;
     L.max_position = -1;
     L.useful_pairs = 0;
     L.unpacked_pairs = 0;
@@ -154,7 +158,9 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
         L.tok_g0[t] = g0;
         L.tok_pe[t] = pe;
         L.tok_ss[t] = g0;
+        L.tok_owner[t] = g;
       }
+      L.max_prefix_len = std::max(L.max_prefix_len, P);
       if (P > 0) L.max_position = std::max(L.max_position, P - 1);
       const int64_t Pl = P;
       L.useful_pairs += Pl * (Pl + 1) / 2;
@@ -167,7 +173,10 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
           L.tok_g0[t] = g0;
           L.tok_pe[t] = pe;
           L.tok_ss[t] = cur;
+          L.tok_owner[t] = int32_t(k);
         }
+        L.suffix_group[size_t(k)] = g;
+        L.max_suffix_len = std::max(L.max_suffix_len, S);
         if (S > 0) L.max_position = std::max(L.max_position, P + S - 1);
         const int64_t Sl = S;
         L.useful_pairs += Sl * Pl + Sl * (Sl + 1) / 2;

@@ -311,3 +311,15 @@ def test_backward_needs_bf16_d128_and_an_uploaded_layout():
     args = [dummy] * 10
     assert lib.pg_attn_bwd(L.handle, *args, 1, ctypes.c_float(0.1), None) == -5   # not uploaded
     assert lib.pg_attn_bwd(None, *args, 1, ctypes.c_float(0.1), None) == -1
+
+
+def test_pack_and_unpack_argument_errors():
+    lib = _lib.load()
+    L = _build([5], [[3]])
+    dummy = ctypes.c_void_p(16)
+    # not uploaded yet
+    assert lib.pg_pack_rows(L.handle, dummy, 8, dummy, 8, dummy, 16, None) == -5
+    assert lib.pg_unpack_rows(L.handle, dummy, 16, dummy, 8, dummy, 8, None) == -5
+    E = _build([], [])   # no tokens: argument checks still apply
+    assert lib.pg_pack_rows(E.handle, None, 0, None, 0, None, 6, None) == -1   # not a multiple of 4
+    assert lib.pg_unpack_rows(E.handle, None, 0, None, 0, None, 0, None) == -1
