@@ -283,7 +283,7 @@ def main(argv=None):
             pg.pg_pack_rows(L, pre, suf, packed=packed, stream=stream)
             pg.pg_unpack_rows(L, packed, ppad, spad, stream=stream)
         tp, tu = [], []
-        for _ in range(max(3, args.steps // 2)):
+        for _ in range(20):
             a_, b_, c_ = ev(), ev(), ev()
             a_.record(stream)
             pg.pg_pack_rows(L, pre, suf, packed=packed, stream=stream)
@@ -292,7 +292,18 @@ def main(argv=None):
             c_.record(stream)
             tp.append((a_, b_))
             tu.append((b_, c_))
+        # a plain device copy of the packed bytes: the practical ceiling
+        cpy = torch.empty_like(packed)
+        tc = []
+        for _ in range(20):
+            a_, b_ = ev(), ev()
+            a_.record(stream)
+            with torch.cuda.stream(stream):
+                cpy.copy_(packed)
+            b_.record(stream)
+            tc.append((a_, b_))
         torch.cuda.synchronize()
+        cms = float(np.mean([x.elapsed_time(y) for x, y in tc]))
         pms = float(np.mean([x.elapsed_time(y) for x, y in tp]))
         ums = float(np.mean([x.elapsed_time(y) for x, y in tu]))
         rb = hidden * 2
@@ -301,9 +312,10 @@ def main(argv=None):
         gathers = {"row_bytes": rb,
                    "pack_ms": round(pms, 4), "pack_gbs": round(pack_bytes / (pms * 1e-3) / 1e9, 1),
                    "unpack_ms": round(ums, 4), "unpack_gbs": round(unpack_bytes / (ums * 1e-3) / 1e9, 1),
+                   "device_copy_gbs": round(pack_bytes / (cms * 1e-3) / 1e9, 1),
                    "hbm_peak_gbs": PEAK_HBM_GBS}
         L.close()
-        del pre, suf, packed, outs
+        del pre, suf, packed, outs, cpy
 
     traffic = load_traffic(w.name)
     roof = {

@@ -22,7 +22,7 @@
 //  * bwd_dkv_kernel: key blocks of at most 128 keys of one KV head inside one
 //    segment. The queries that read key j are one contiguous range [j, qend)
 //    (the group's end for a prompt key, the response's end otherwise), taken
-//    in tiles of 32 rows for each of the r query heads. Per wave 32 keys:
+//    in tiles of 64 rows for each of the r query heads. Per wave 32 keys:
 //      S = Q K^T, dP = dO V^T                (A = Q, dO rows from LDS)
 //      P, dS as above (lse and D per query row from LDS)
 //      dV += P^T dO, dK += dS^T Q           (A = P^T, dS^T from the
@@ -31,7 +31,7 @@
 //    so K, V, dK and dV stay in registers for the whole block and no atomics
 //    are needed.
 // Tiles go HBM -> LDS with buffer loads that write LDS (as in the forward),
-// three stages deep, with one workgroup barrier per tile.
+// four (dQ) or three (dK, dV) stages deep, with one workgroup barrier per tile.
 #include <hip/hip_runtime.h>
 
 #include "pg_hip_common.h"

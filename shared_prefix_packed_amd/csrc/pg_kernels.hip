@@ -213,7 +213,31 @@ __global__ __launch_bounds__(64) void attn_rowwise_kernel(
 // page, sections 2-3: concatenating each prompt once with its responses, and
 // splitting the output back with the last prompt position included in each
 // response part). A row is `upr` units of U (16 bytes when the row size
-// allows, else 4); consecutive threads move consecutive units of a row.
+// allows, else 4). One wave per row (grid-stride over rows): the row's source
+// is resolved once from the token tables, then consecutive lanes move
+// consecutive units, GATHER_UNROLL loads in flight per lane before the stores.
+constexpr int GATHER_UNROLL = 4;
+
+template <typename U>
+__device__ __forceinline__ void copy_row(const U* __restrict__ src, U* __restrict__ dst,
+                                         int64_t upr, int lane) {
+  int64_t c = lane;
+  for (; c + 64 * (GATHER_UNROLL - 1) < upr; c += 64 * GATHER_UNROLL) {
+    U v[GATHER_UNROLL];
+#pragma unroll
+    for (int i = 0; i < GATHER_UNROLL; ++i) v[i] = src[c + 64 * i];
+#pragma unroll
+    for (int i = 0; i < GATHER_UNROLL; ++i) dst[c + 64 * i] = v[i];
+  }
+  for (; c < upr; c += 64) dst[c] = src[c];
+}
+
+template <typename U>
+__device__ __forceinline__ void zero_row(U* __restrict__ dst, int64_t upr, int lane) {
+  U z;
+  __builtin_memset(&z, 0, sizeof(U));
+  for (int64_t c = lane; c < upr; c += 64) dst[c] = z;
+}
 
 // packed[t] = prompt row (owner g, index t - g0) or response row (owner k,
 // index t - ss).
@@ -225,14 +249,14 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const int32_t* __restric
                                                         const U* prefix, int64_t ppad,
                                                         const U* suffix, int64_t spad, U* packed,
                                                         int64_t rows, int64_t upr) {
-  const int64_t total = rows * upr;
-  for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
-       u += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t t = u / upr, c = u - t * upr;
-    const int32_t o = owner[t];
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x >> 6);
+  for (int64_t t = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); t < rows;
+       t += nw) {
+    const int64_t o = owner[t];
     const U* src = t < pe[t] ? prefix + (o * ppad + (t - g0[t])) * upr
                              : suffix + (o * spad + (t - ss[t])) * upr;
-    packed[u] = src[c];
+    copy_row(src, packed + t * upr, upr, lane);
   }
 }
 
@@ -248,11 +272,12 @@ __global__ __launch_bounds__(256) void unpack_rows_kernel(
     int64_t ppad, U* suffix_out, int64_t N, int64_t spad, int64_t upr) {
   const int64_t pre_rows = prefix_out ? G * ppad : 0;
   const int64_t suf_rows = suffix_out ? N * (spad + 1) : 0;
-  const int64_t total = (pre_rows + suf_rows) * upr;
+  const int64_t rows = pre_rows + suf_rows;
   const bool have = group_off != nullptr;
-  for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
-       u += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t row = u / upr, c = u - row * upr;
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x >> 6);
+  for (int64_t row = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); row < rows;
+       row += nw) {
     int64_t src = -1;
     U* dst;
     if (row < pre_rows) {
@@ -272,13 +297,10 @@ __global__ __launch_bounds__(256) void unpack_rows_kernel(
       }
       dst = suffix_out + r * upr;
     }
-    U val;
-    if (src >= 0) {
-      val = packed[src * upr + c];
-    } else {
-      __builtin_memset(&val, 0, sizeof(U));
-    }
-    dst[c] = val;
+    if (src >= 0)
+      copy_row(packed + src * upr, dst, upr, lane);
+    else
+      zero_row(dst, upr, lane);
   }
 }
 
@@ -329,10 +351,10 @@ hipError_t pg_launch_attn_rowwise(const pg_layout& L, const void* q, const void*
 }
 
 namespace {
-// grid for a grid-stride loop over `units` threads' worth of work
-dim3 gather_grid(int64_t units) {
-  const int64_t blocks = (units + 255) / 256;
-  return dim3(uint32_t(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536));
+// Four rows (waves) per 256-thread block, at most 8192 blocks (32 waves per CU).
+dim3 gather_grid(int64_t rows) {
+  const int64_t blocks = (rows + 3) / 4;
+  return dim3(uint32_t(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192));
 }
 }  // namespace
 
@@ -342,12 +364,12 @@ hipError_t pg_launch_pack(const pg_layout& L, const void* prefix, int32_t prefix
   if (L.T == 0) return hipSuccess;
   if (row_bytes % 16 == 0) {
     const int64_t upr = row_bytes / 16;
-    pack_rows_kernel<uint4><<<gather_grid(L.T * upr), dim3(256), 0, stream>>>(
+    pack_rows_kernel<uint4><<<gather_grid(L.T), dim3(256), 0, stream>>>(
         L.d_owner, L.d_g0, L.d_pe, L.d_ss, static_cast<const uint4*>(prefix), prefix_pad,
         static_cast<const uint4*>(suffix), suffix_pad, static_cast<uint4*>(packed), L.T, upr);
   } else {
     const int64_t upr = row_bytes / 4;
-    pack_rows_kernel<uint32_t><<<gather_grid(L.T * upr), dim3(256), 0, stream>>>(
+    pack_rows_kernel<uint32_t><<<gather_grid(L.T), dim3(256), 0, stream>>>(
         L.d_owner, L.d_g0, L.d_pe, L.d_ss, static_cast<const uint32_t*>(prefix), prefix_pad,
         static_cast<const uint32_t*>(suffix), suffix_pad, static_cast<uint32_t*>(packed), L.T,
         upr);
@@ -362,11 +384,16 @@ hipError_t pg_launch_unpack(const pg_layout& L, const void* packed, int64_t row_
   const int64_t rows = (prefix_out ? G * prefix_pad : 0) + (suffix_out ? N * (suffix_pad + 1) : 0);
   if (rows == 0) return hipSuccess;
   const bool have = L.T > 0;   // a layout without tokens has no device tables: all zeros
-#define PG_UNPACK(U, W)                                                                            unpack_rows_kernel<U><<<gather_grid(rows * (row_bytes / W)), dim3(256), 0, stream>>>(              have ? L.d_group_off : nullptr, L.d_prefix_lens, L.d_seg_off, L.d_suffix_group,                L.d_suffix_lens, static_cast<const U*>(packed), static_cast<U*>(prefix_out), G,                 prefix_pad, static_cast<U*>(suffix_out), N, suffix_pad, row_bytes / W)
+  const int32_t* go = have ? L.d_group_off : nullptr;
   if (row_bytes % 16 == 0)
-    PG_UNPACK(uint4, 16);
+    unpack_rows_kernel<uint4><<<gather_grid(rows), dim3(256), 0, stream>>>(
+        go, L.d_prefix_lens, L.d_seg_off, L.d_suffix_group, L.d_suffix_lens,
+        static_cast<const uint4*>(packed), static_cast<uint4*>(prefix_out), G, prefix_pad,
+        static_cast<uint4*>(suffix_out), N, suffix_pad, row_bytes / 16);
   else
-    PG_UNPACK(uint32_t, 4);
-#undef PG_UNPACK
+    unpack_rows_kernel<uint32_t><<<gather_grid(rows), dim3(256), 0, stream>>>(
+        go, L.d_prefix_lens, L.d_seg_off, L.d_suffix_group, L.d_suffix_lens,
+        static_cast<const uint32_t*>(packed), static_cast<uint32_t*>(prefix_out), G, prefix_pad,
+        static_cast<uint32_t*>(suffix_out), N, suffix_pad, row_bytes / 4);
   return hipGetLastError();
 }
