@@ -31,6 +31,8 @@ Readings where the pages are silent (each listed in the design doc):
 
 The backward (``attention_backward``) is the chain rule of that definition
 written out for an upstream gradient of O; tests/test_oracle_backward.py pins it.
+``decode_attention`` is one generation step over a group-contiguous cache;
+tests/test_oracle_decode.py pins it.
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (hand-derived values, closed forms, a library routine, brute
@@ -546,6 +548,82 @@ def unpack_rows(packed: np.ndarray, lay, prefix_pad: int, suffix_pad: int):
             cur += S
             k += 1
     return pre, suf
+
+
+# ------------------------------------------------------------------ decode --
+
+
+def decode_key_rows(lay, cur_lens, k: int) -> np.ndarray:
+    """Cache rows that response k's newest token attends to at a decode step.
+
+    PackInfer abstract (I/O-aware grouping): requests that share a prefix are
+    co-located and their KV cache is kept group-contiguous while generation
+    proceeds, so the prompt's keys are stored, and read, once per group.
+    Reading: the cache is the packed layout of ``lay`` with each response's
+    segment at its capacity (``lay``'s suffix_lens); response k's valid rows
+    are the first len_k = clamp(cur_lens[k], 0, capacity_k) of its segment, the
+    last of them holding the token being decoded. Its key set is the group's
+    prompt rows plus its own valid rows; a sibling's rows are never read.
+    """
+    g = int(response_group(lay)[k])
+    a = int(lay["group_off"][g])
+    P = int(lay["prefix_lens"][g])
+    s0 = int(lay["seg_off"][g + k + 1])          # segments: per group prefix, then responses
+    cap = int(lay["suffix_lens"][k])
+    n = min(max(int(cur_lens[k]), 0), cap)
+    return np.concatenate([np.arange(a, a + P), np.arange(s0, s0 + n)]).astype(np.int64)
+
+
+def response_group(lay) -> np.ndarray:
+    """Group of each response, responses in group order."""
+    return np.repeat(np.arange(len(lay["prefix_lens"])), lay["suffix_counts"]).astype(np.int64)
+
+
+def decode_attention(q, k_cache, v_cache, lay, cur_lens, scale: float,
+                     num_q_heads: int, num_kv_heads: int):
+    """One decode step of shared-prefix attention: the newest token of every
+    response attends to its group's prompt and its own rows so far.
+
+    q: [N, Hq, d], one query per response (responses in group order);
+    k_cache, v_cache: [T, Hkv, d] in the layout's order; cur_lens: [N].
+    Written out by definition: softmax of the scaled scores over
+    ``decode_key_rows``, times V, in fp64. An empty key set (no prompt and no
+    valid row) gives o = 0 and lse = -inf (reading).
+    Returns o [N, Hq, d] and lse [Hq, N] (natural log, scaled scores).
+    Pinned by: the forward oracle's last row of each response on the compacted
+    layout (tests/test_oracle_decode.py), torch's float64 SDPA per response,
+    closed forms (one key, constant V, empty set) and a planted sibling leak.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    N, Hq, d = q.shape
+    o = np.zeros((N, Hq, d), dtype=np.float64)
+    lse = np.full((Hq, N), -np.inf, dtype=np.float64)
+    for k in range(N):
+        rows = decode_key_rows(lay, cur_lens, k)
+        if len(rows) == 0:
+            continue
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, num_kv_heads)
+            s = scale * (kc[rows, hk] @ q[k, h])
+            m = s.max()
+            p = np.exp(s - m)
+            o[k, h] = (p @ vc[rows, hk]) / p.sum()
+            lse[h, k] = m + np.log(p.sum())
+    return o, lse
+
+
+def decode_bytes(lay, cur_lens, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """K and V bytes one decode step must read: each group's prompt once plus
+    every response's valid rows (the I/O PackInfer's grouping aims at)."""
+    rows = 0
+    for g in range(len(lay["prefix_lens"])):
+        if int(lay["suffix_counts"][g]) > 0:
+            rows += int(lay["prefix_lens"][g])
+    caps = np.asarray(lay["suffix_lens"], dtype=np.int64)
+    rows += int(np.clip(np.asarray(cur_lens, dtype=np.int64), 0, caps).sum())
+    return rows * num_kv_heads * head_dim * elem_bytes * 2
 
 
 # ---------------------------------------------------------- FLOP accounting --

@@ -12,6 +12,7 @@ from .synth import (  # noqa: F401
     make_custom,
     draw_tensor,
     draw_qkv,
+    draw_decode,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     sha256,

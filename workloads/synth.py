@@ -182,6 +182,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 _STREAM = {"q": 1, "k": 2, "v": 3, "do": 4}   # "do": upstream gradient of O (backward)
+_DECODE_STREAM = 5                                # decode step: current lengths, then queries
 
 
 def draw_tensor(w: Workload, which: str, chunk_tokens: int = 4096) -> np.ndarray:
@@ -207,6 +208,27 @@ def draw_tensor(w: Workload, which: str, chunk_tokens: int = 4096) -> np.ndarray
         x = rng.standard_normal((t1 - t0) * row, dtype=np.float32).reshape(t1 - t0, row)
         flat[t0:t1] = x if w.dtype == "f32" else f32_to_bf16_bits(x)
     return out
+
+
+def draw_decode(w: Workload) -> Dict[str, np.ndarray]:
+    """Inputs of one decode step over workload ``w``'s layout taken as a KV
+    cache whose response segments are at capacity (the drawn suffix lengths).
+
+    cur_lens: int32 [N], uniform on [min(1, cap), cap] per response (the step
+    falls anywhere in generation); q: [N, Hq, d], one query per response, drawn
+    like Q (float32 N(0,1); uint16 bf16 bits for bf16 workloads).
+    """
+    if w.index >= 0:
+        rng = _rng(w.index, _DECODE_STREAM, w.seed)
+    else:
+        rng = np.random.default_rng([1000, _DECODE_STREAM, int(w.seed or 0)])
+    caps = np.asarray(w.suffix_lens, dtype=np.int64)
+    lo = np.minimum(caps, 1)
+    cur = (lo + np.floor(rng.random(len(caps)) * (caps - lo + 1))).astype(np.int32)
+    n, hq, d = len(caps), w.num_q_heads, w.head_dim
+    x = rng.standard_normal(n * hq * d, dtype=np.float32).reshape(n, hq, d)
+    q = x if w.dtype == "f32" else f32_to_bf16_bits(x)
+    return {"cur_lens": cur, "q": q}
 
 
 def draw_qkv(w: Workload) -> Dict[str, np.ndarray]:
