@@ -62,57 +62,6 @@ __device__ inline void buf4_to_lds(i32x4_t r, int voff, uint32_t lds) {
       : "memory");
 }
 
-// Byte offset (from a tile's first row) of the 16-byte global unit that lane
-// `lane` of 1 KB block `b` brings into a row-major tile: row 4 b + lane / 16,
-// stored chunk lane % 16 holding global chunk (lane % 16) ^ (row % 16).
-__device__ inline int rowmajor_off(int b, int lane, int row_bytes) {
-  const int row = 4 * b + (lane >> 4);
-  const int chunk = (lane & 15) ^ (row & 15);
-  return row * row_bytes + 16 * chunk;
-}
-
-// Lane offsets of the transposing reads that take MFMA operand fragments out
-// of a row-major tile (256-byte rows, 16-byte chunks XOR-swizzled by row % 16):
-// within each 16-lane group the lanes address a 4-row x 32-byte block, lane
-// 4 j + c pointing at 4 columns 4c..4c+3 of row j, so that lane n receives
-// column n of the 4 rows. For the 16-row step s (rows 16 s + 4 (lane / 32) +
-// 0..3, then + 8: the accumulators' row order) and column block db the two
-// reads sit at tile + 4096 s + lo[db] and + hi[db]; row % 16 does not depend
-// on s, so neither does the swizzle.
-struct TrOffsets {
-  int lo[4], hi[4];
-  __device__ explicit TrOffsets(int lane) {
-    const int rlo = 4 * (lane >> 5) + ((lane >> 2) & 3);
-    const int rhi = rlo + 8;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int byte = 64 * db + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-      const int c16 = byte >> 4, within = byte & 15;
-      lo[db] = rlo * 256 + 16 * (c16 ^ (rlo & 15)) + within;
-      hi[db] = rhi * 256 + 16 * (c16 ^ (rhi & 15)) + within;
-    }
-  }
-};
-
-__device__ inline bf16x8_t tr_rowmajor(const unsigned char* tile, const TrOffsets& o, int s, int db) {
-  const i16x4_t lo = lds_read_tr(tile + 4096 * s + o.lo[db]);
-  const i16x4_t hi = lds_read_tr(tile + 4096 * s + o.hi[db]);
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Accumulator registers of a 32x32 block (row 8 (i/4) + 4 half + i%4) packed
-// as the operand of the 16-row step s (rows 16 s .. 16 s + 15): registers
-// 8 (s & 1) + 0..7 of block s / 2.
-__device__ inline bf16x8_t pack_step(const f32x16_t& c, int s) {
-  uint4 pk;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int i = 8 * (s & 1) + 2 * jj;
-    (&pk.x)[jj] = pack_bf16x2(c[i], c[i + 1]);
-  }
-  return as_bf16x8(pk);
-}
-
 // Writes a 32 x 128 fp32 tile held as four 32x32 accumulator blocks (block db
 // covers d = 32 db .. 32 db + 31), scaled by `mul` and rounded to bf16,
 // through LDS region `ot` (8 KB, 16-byte chunks XOR-swizzled by row) to the
@@ -263,9 +212,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
       dof[ks] = as_bf16x8(ldg16(a.dout + base + 16 * ks));
     }
   }
-  const float lse2 = a.lse[int64_t(h) * a.T + tq] * LOG2E;
-  const float dlt = a.delta[int64_t(h) * a.T + tq];
-  const int ss_t = a.tok_ss[tq];
+  float lse2 = a.lse[int64_t(h) * a.T + tq] * LOG2E;
+  float dlt = a.delta[int64_t(h) * a.T + tq];
+  int ss_t = a.tok_ss[tq];
+  // Redefine the loaded values by an empty asm: the compiler waits for their
+  // loads once, here. Counted inside the tile loop instead, next to the tile
+  // fetches it cannot see, its waits would drain every tile in flight.
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qf[ks]), "+v"(dof[ks]));
+  asm volatile("" : "+v"(lse2), "+v"(dlt), "+v"(ss_t));
   const int ss_max = ld_scalar(a.tok_ss, wave_active ? te - 1 : it.t0);
 
   int ntiles = 0;
@@ -442,6 +397,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
       kf[ks] = as_bf16x8(zk);
       vf[ks] = as_bf16x8(zv);
     }
+    // waited for once, here, not inside the tile loop (see bwd_dq_kernel)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(kf[ks]), "+v"(vf[ks]));
   }
 
   f32x16_t dkacc[4], dvacc[4];

@@ -1,6 +1,7 @@
-// Device helpers shared by the attention kernels of libpg.so (forward and
-// backward): operand types, buffer->LDS loads, transposing LDS reads, bf16
-// packing, wait counters and MFMA/LDS-read scheduling patterns. gfx950 only.
+// Device helpers shared by the attention kernels of libpg.so (forward,
+// backward, decode): operand types, buffer->LDS loads, transposing LDS reads,
+// bf16 packing, wait counters, MFMA/LDS-read scheduling patterns and the
+// row-major swizzled tile addressing. gfx950 only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -84,12 +85,12 @@ __device__ inline int ld_scalar(const void* base, int i) {
   return __builtin_amdgcn_readfirstlane(c[i]);
 }
 
-// s_waitcnt vmcnt(N) for N < 16 (gfx9 encoding: expcnt and lgkmcnt fields
-// left at "no wait").
+// s_waitcnt vmcnt(N) for N < 64 (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt and lgkmcnt fields left at "no wait").
 template <int N>
 __device__ inline void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 // s_waitcnt lgkmcnt(0) (vmcnt and expcnt fields at "no wait").
 __device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -118,6 +119,59 @@ template <int AHEAD, int PER, int NM>
 __device__ inline void sched_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
   sched_mfma_then_reads<0, NM, PER, NM * PER - AHEAD>();
+}
+
+// ------------------------------------------- row-major tiles of 256-byte rows --
+
+// Byte offset (from a tile's first row) of the 16-byte global unit that lane
+// `lane` of 1 KB block `b` brings into a row-major tile: row 4 b + lane / 16,
+// stored chunk lane % 16 holding global chunk (lane % 16) ^ (row % 16).
+__device__ inline int rowmajor_off(int b, int lane, int row_bytes) {
+  const int row = 4 * b + (lane >> 4);
+  const int chunk = (lane & 15) ^ (row & 15);
+  return row * row_bytes + 16 * chunk;
+}
+
+// Lane offsets of the transposing reads that take MFMA operand fragments out
+// of a row-major tile (256-byte rows, 16-byte chunks XOR-swizzled by row % 16):
+// within each 16-lane group the lanes address a 4-row x 32-byte block, lane
+// 4 j + c pointing at 4 columns 4c..4c+3 of row j, so that lane n receives
+// column n of the 4 rows. For the 16-row step s (rows 16 s + 4 (lane / 32) +
+// 0..3, then + 8: the accumulators' row order) and column block db the two
+// reads sit at tile + 4096 s + lo[db] and + hi[db]; row % 16 does not depend
+// on s, so neither does the swizzle.
+struct TrOffsets {
+  int lo[4], hi[4];
+  __device__ explicit TrOffsets(int lane) {
+    const int rlo = 4 * (lane >> 5) + ((lane >> 2) & 3);
+    const int rhi = rlo + 8;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int byte = 64 * db + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+      const int c16 = byte >> 4, within = byte & 15;
+      lo[db] = rlo * 256 + 16 * (c16 ^ (rlo & 15)) + within;
+      hi[db] = rhi * 256 + 16 * (c16 ^ (rhi & 15)) + within;
+    }
+  }
+};
+
+__device__ inline bf16x8_t tr_rowmajor(const unsigned char* tile, const TrOffsets& o, int s, int db) {
+  const i16x4_t lo = lds_read_tr(tile + 4096 * s + o.lo[db]);
+  const i16x4_t hi = lds_read_tr(tile + 4096 * s + o.hi[db]);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Accumulator registers of a 32x32 block (row 8 (i/4) + 4 half + i%4) packed
+// as the operand of the 16-row step s (rows 16 s .. 16 s + 15): registers
+// 8 (s & 1) + 0..7 of block s / 2.
+__device__ inline bf16x8_t pack_step(const f32x16_t& c, int s) {
+  uint4 pk;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int i = 8 * (s & 1) + 2 * jj;
+    (&pk.x)[jj] = pack_bf16x2(c[i], c[i + 1]);
+  }
+  return as_bf16x8(pk);
 }
 
 }  // namespace pg_hip
