@@ -29,6 +29,7 @@
 #ifndef PG_H
 #define PG_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -70,7 +71,8 @@ typedef struct pg_layout_summary {
   int64_t max_item_cost;   /* largest work item, in (query, key) pairs x heads   */
   int64_t max_xcd_cost;    /* largest per-XCD sum of item costs (balance check)  */
   int32_t num_kv_items;    /* work items of the backward dK/dV launch            */
-  int32_t reserved;        /* 0                                                  */
+  int32_t num_dec_items;   /* work items of the decode launch (padding included) */
+  int64_t num_dec_refs;    /* entries of the decode merge lists                  */
 } pg_layout_summary;
 
 /* One work item of the attention launch: query tokens [t0, t1) of one group,
@@ -102,6 +104,25 @@ typedef struct pg_kv_item {
   int32_t qend;
   int64_t cost;   /* (query, key) pairs of the item x the r query heads      */
 } pg_kv_item;
+
+/* One work item of the decode launch (pg_attn_decode): cache rows [k0, k1) of
+ * KV head hk inside one segment [seg0, seg1) of the layout -- a prompt
+ * (resp = -1) or the segment of response `resp` at its capacity -- for the
+ * query rows [row0, row0 + nrow), at most 32, where query row k * r + i is
+ * query head hk * r + i of response k (r = Hq / Hkv). A prompt item carries
+ * rows of the group's responses, a response item only rows of its own
+ * response and stops, at run time, at that response's current length.
+ * Launch order as pg_work_item (XCD p % 8); nrow == 0 marks padding. */
+typedef struct pg_dec_item {
+  int32_t k0;
+  int32_t k1;
+  int32_t hk;
+  int32_t resp;
+  int32_t seg0;
+  int32_t seg1;
+  int32_t row0;
+  int32_t nrow;
+} pg_dec_item;
 
 /* A contiguous key range [k0, k1) inside one segment of one group. */
 typedef struct pg_key_span {
@@ -177,6 +198,13 @@ pg_status pg_layout_copy_work(const pg_layout* layout, pg_work_item* items, pg_k
 
 /* Host copy of the backward dK/dV work list: items [num_kv_items]. */
 pg_status pg_layout_copy_kv_work(const pg_layout* layout, pg_kv_item* items);
+
+/* Host copy of the decode work list: items [num_dec_items] (launch order),
+ * ref_off [N * Hkv + 1] and refs [num_dec_refs]: the items whose rows include
+ * response k's query heads of KV head hk are refs[ref_off[k * Hkv + hk] ..
+ * ref_off[k * Hkv + hk + 1]) (indices into items). Any pointer may be NULL. */
+pg_status pg_layout_copy_decode_work(const pg_layout* layout, pg_dec_item* items,
+                                     int32_t* ref_off, int32_t* refs);
 
 /* Free the layout. Returns at once: its upload buffer goes back to the cache
  * and is reused only after the work already enqueued with this layout has
@@ -290,6 +318,46 @@ pg_status pg_attn_bwd(const pg_layout* layout, const void* q, const void* k, con
                       const void* o, const float* lse, const void* dout, void* dq, void* dk,
                       void* dv, float* delta, pg_dtype dtype, float softmax_scale,
                       hipStream_t stream);
+
+/*
+ * pg_decode_workspace_size -- bytes of device scratch pg_attn_decode needs on
+ * this layout: one fp32 partial result (32 rows x (d + 2) floats) per decode
+ * work item. 0 for a layout without responses.
+ */
+pg_status pg_decode_workspace_size(const pg_layout* layout, size_t* bytes);
+
+/*
+ * pg_attn_decode -- one decode step of shared-prefix attention over a
+ * group-contiguous KV cache (PackInfer abstract: I/O-aware grouping co-locates
+ * requests that share a prefix and keeps their KV cache group-contiguous as
+ * generation proceeds, so a prompt's keys are read once per group per step).
+ *
+ * The cache is the layout's packed order with every response segment at its
+ * capacity: build the layout with suffix_lens = the capacities. Response k's
+ * first len_k = clamp(cur_lens[k], 0, capacity_k) rows are valid, the last of
+ * them holding the token being decoded (its K and V already written). Its
+ * query attends to the group's prompt rows and its own valid rows, never to a
+ * sibling's.
+ *  q          [N, Hq, d], the query of each response's newest token (N =
+ *             sum(suffix_counts), responses in group order)
+ *  k_cache, v_cache  [T, Hkv, d]
+ *  cur_lens   device int32 [N]; read on the device, so a decode loop updates it
+ *             without a host round trip
+ *  o          [N, Hq, d], written completely (zero for an empty key set)
+ *  lse        fp32 [Hq, N], natural log of the scaled scores' exp sum (-inf for
+ *             an empty key set)
+ *  workspace  device scratch of workspace_bytes >= pg_decode_workspace_size
+ *             bytes (used by the bf16, d = 128 kernel; other dtypes and d = 64
+ *             run one workgroup per output row and leave it untouched, and
+ *             may pass NULL)
+ * Device pointers; all tensors share dtype. Calls that share a workspace must
+ * not overlap. PG_ERR_INVALID_ARG on NULL tensors, a short workspace or a bad
+ * scale.
+ */
+pg_status pg_attn_decode(const pg_layout* layout, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* cur_lens, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, pg_dtype dtype,
+                         float softmax_scale, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* pg_status_string(pg_status status);

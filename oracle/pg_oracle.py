@@ -580,7 +580,7 @@ def response_group(lay) -> np.ndarray:
 
 
 def decode_attention(q, k_cache, v_cache, lay, cur_lens, scale: float,
-                     num_q_heads: int, num_kv_heads: int):
+                     num_q_heads: int, num_kv_heads: int, responses=None):
     """One decode step of shared-prefix attention: the newest token of every
     response attends to its group's prompt and its own rows so far.
 
@@ -589,27 +589,28 @@ def decode_attention(q, k_cache, v_cache, lay, cur_lens, scale: float,
     Written out by definition: softmax of the scaled scores over
     ``decode_key_rows``, times V, in fp64. An empty key set (no prompt and no
     valid row) gives o = 0 and lse = -inf (reading).
-    Returns o [N, Hq, d] and lse [Hq, N] (natural log, scaled scores).
+    Returns o [N, Hq, d] and lse [Hq, N] (natural log, scaled scores);
+    with ``responses`` given, only those rows are computed (the rest stay 0).
     Pinned by: the forward oracle's last row of each response on the compacted
     layout (tests/test_oracle_decode.py), torch's float64 SDPA per response,
     closed forms (one key, constant V, empty set) and a planted sibling leak.
     """
     q = np.asarray(q, dtype=np.float64)
-    kc = np.asarray(k_cache, dtype=np.float64)
-    vc = np.asarray(v_cache, dtype=np.float64)
     N, Hq, d = q.shape
     o = np.zeros((N, Hq, d), dtype=np.float64)
     lse = np.full((Hq, N), -np.inf, dtype=np.float64)
-    for k in range(N):
+    for k in (range(N) if responses is None else responses):
         rows = decode_key_rows(lay, cur_lens, k)
         if len(rows) == 0:
             continue
+        kc = np.asarray(k_cache[rows], dtype=np.float64)
+        vc = np.asarray(v_cache[rows], dtype=np.float64)
         for h in range(Hq):
             hk = _kv_head(h, Hq, num_kv_heads)
-            s = scale * (kc[rows, hk] @ q[k, h])
+            s = scale * (kc[:, hk] @ q[k, h])
             m = s.max()
             p = np.exp(s - m)
-            o[k, h] = (p @ vc[rows, hk]) / p.sum()
+            o[k, h] = (p @ vc[:, hk]) / p.sum()
             lse[h, k] = m + np.log(p.sum())
     return o, lse
 

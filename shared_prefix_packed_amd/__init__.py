@@ -7,6 +7,7 @@ its Python binding; importing it loads nothing until a function is called.
 from .api import (  # noqa: F401
     Layout,
     pg_attn_bwd,
+    pg_attn_decode,
     pg_attn_fwd,
     pg_build_layout,
     pg_build_layout_host,

@@ -36,7 +36,8 @@ class LayoutSummary(ctypes.Structure):
         ("max_item_cost", c_int64),
         ("max_xcd_cost", c_int64),
         ("num_kv_items", c_int32),
-        ("reserved", c_int32),
+        ("num_dec_items", c_int32),
+        ("num_dec_refs", ctypes.c_int64),
     ]
 
 
@@ -47,6 +48,11 @@ class WorkItem(ctypes.Structure):
 
 class KeySpan(ctypes.Structure):
     _fields_ = [("k0", c_int32), ("k1", c_int32)]
+
+
+class DecItem(ctypes.Structure):
+    _fields_ = [("k0", c_int32), ("k1", c_int32), ("hk", c_int32), ("resp", c_int32),
+                ("seg0", c_int32), ("seg1", c_int32), ("row0", c_int32), ("nrow", c_int32)]
 
 
 class KvItem(ctypes.Structure):
@@ -67,6 +73,11 @@ SIGNATURES = {
     "pg_layout_copy_work": (c_int32, [c_void_p, ctypes.POINTER(WorkItem),
                                       ctypes.POINTER(KeySpan)]),
     "pg_layout_copy_kv_work": (c_int32, [c_void_p, ctypes.POINTER(KvItem)]),
+    "pg_layout_copy_decode_work": (c_int32, [c_void_p, ctypes.POINTER(DecItem), P_int32, P_int32]),
+    "pg_decode_workspace_size": (c_int32, [c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
+    "pg_attn_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, ctypes.c_size_t, c_int32, ctypes.c_float,
+                                 c_void_p]),
     "pg_layout_destroy": (None, [c_void_p]),
     "pg_position_ids": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "pg_rope": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,

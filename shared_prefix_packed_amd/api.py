@@ -12,7 +12,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import KeySpan, KvItem, LayoutSummary, WorkItem, check, load
+from ._lib import DecItem, KeySpan, KvItem, LayoutSummary, WorkItem, check, load
 
 
 def _i32(x) -> np.ndarray:
@@ -101,6 +101,33 @@ class Layout:
         it = np.frombuffer(items, dtype=np.dtype([("k0", "<i4"), ("k1", "<i4"), ("hk", "<i4"),
                                                   ("qend", "<i4"), ("cost", "<i8")]))
         return it[:s.num_kv_items].copy()
+
+    @property
+    def num_responses(self) -> int:
+        s = self.summary()
+        return s.num_segments - s.num_groups
+
+    def decode_work(self) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Decode work items (structured array, launch order), the merge-list
+        offsets [N * Hkv + 1] and the merge lists (item indices)."""
+        s = self.summary()
+        n_off = self.num_responses * self.num_kv_heads + 1
+        items = (DecItem * max(1, s.num_dec_items))()
+        off = np.zeros(max(1, n_off), dtype=np.int32)
+        refs = np.zeros(max(1, s.num_dec_refs), dtype=np.int32)
+        check(load().pg_layout_copy_decode_work(self.handle, items, _ptr_i32(off), _ptr_i32(refs)),
+              "pg_layout_copy_decode_work")
+        it = np.frombuffer(items, dtype=np.dtype([(n, "<i4") for n in
+                                                  ("k0", "k1", "hk", "resp", "seg0", "seg1",
+                                                   "row0", "nrow")]))
+        return it[:s.num_dec_items].copy(), off[:n_off].copy(), refs[:s.num_dec_refs].copy()
+
+    def decode_workspace_size(self) -> int:
+        """Bytes of device scratch pg_attn_decode needs on this layout."""
+        n = ctypes.c_size_t(0)
+        check(load().pg_decode_workspace_size(self.handle, ctypes.byref(n)),
+              "pg_decode_workspace_size")
+        return int(n.value)
 
 
 def _layout_args(prefix_lens, suffix_counts, suffix_lens):
@@ -248,6 +275,38 @@ def pg_attn_bwd(layout: Layout, q, k, v, o, lse, dout, softmax_scale: float, dq=
                              float(softmax_scale), _stream_handle(stream)),
           "pg_attn_bwd")
     return dq, dk, dv
+
+
+def pg_attn_decode(layout: Layout, q, k_cache, v_cache, cur_lens, softmax_scale: float, o=None,
+                   lse=None, workspace=None, stream=None):
+    """One decode step over a group-contiguous KV cache laid out as ``layout``
+    (response segments at capacity). q: [N, Hq, d], one query per response;
+    cur_lens: device int32 [N]. Returns (o [N, Hq, d], lse fp32 [Hq, N])."""
+    import torch
+    T, Hq, Hkv, d = layout.total_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    N = layout.num_responses
+    _check_tensor("q", q, (N, Hq, d))
+    _check_tensor("k_cache", k_cache, (T, Hkv, d), q.dtype)
+    _check_tensor("v_cache", v_cache, (T, Hkv, d), q.dtype)
+    _check_tensor("cur_lens", cur_lens, (N,), torch.int32)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, (N, Hq, d), q.dtype)
+    _check_tensor("lse", lse, (Hq, N), torch.float32)
+    need = layout.decode_workspace_size()
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    check(load().pg_attn_decode(layout.handle, ptr(q), ptr(k_cache), ptr(v_cache), ptr(cur_lens),
+                                ptr(o), ptr(lse), ptr(workspace), ctypes.c_size_t(ws_bytes),
+                                _dtype_code(q), float(softmax_scale), _stream_handle(stream)),
+          "pg_attn_decode")
+    return o, lse
 
 
 def _row_bytes(t, lead: int) -> int:

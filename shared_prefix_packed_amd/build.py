@@ -23,7 +23,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["pg_layout.cpp", "pg_capi.cpp", "pg_pool.cpp"]
-HIP_SOURCES = ["pg_kernels.hip", "pg_attn_mfma.hip", "pg_attn_bwd.hip"]
+HIP_SOURCES = ["pg_kernels.hip", "pg_attn_mfma.hip", "pg_attn_bwd.hip", "pg_attn_decode.hip"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -108,7 +108,10 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   const size_t off_so = align_up(off_pl + 4 * G, A);
   const size_t off_sg = align_up(off_so + 4 * L->seg_off.size(), A);
   const size_t off_sl = align_up(off_sg + 4 * N, A);
-  const size_t bytes = align_up(off_sl + 4 * N, A);
+  const size_t off_di = align_up(off_sl + 4 * N, A);
+  const size_t off_dro = align_up(off_di + sizeof(pg_dec_item) * L->dec_items.size(), A);
+  const size_t off_dr = align_up(off_dro + 4 * L->dec_ref_off.size(), A);
+  const size_t bytes = align_up(off_dr + 4 * L->dec_refs.size(), A);
   hipError_t e = hipGetDevice(&L->device);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   pg_slot* slot = nullptr;
@@ -133,6 +136,12 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
     std::memcpy(h + off_sg, L->suffix_group.data(), 4 * N);
     std::memcpy(h + off_sl, L->suffix_lens.data(), 4 * N);
   }
+  if (!L->dec_items.empty())
+    std::memcpy(h + off_di, L->dec_items.data(), sizeof(pg_dec_item) * L->dec_items.size());
+  if (!L->dec_ref_off.empty())
+    std::memcpy(h + off_dro, L->dec_ref_off.data(), 4 * L->dec_ref_off.size());
+  if (!L->dec_refs.empty())
+    std::memcpy(h + off_dr, L->dec_refs.data(), 4 * L->dec_refs.size());
   void* d = slot->dev;
   e = hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) {
@@ -156,6 +165,9 @@ pg_status pg_layout_upload(pg_layout* L, hipStream_t stream) {
   L->d_seg_off = reinterpret_cast<const int32_t*>(b + off_so);
   L->d_suffix_group = reinterpret_cast<const int32_t*>(b + off_sg);
   L->d_suffix_lens = reinterpret_cast<const int32_t*>(b + off_sl);
+  L->d_dec_items = reinterpret_cast<const pg_dec_item*>(b + off_di);
+  L->d_dec_ref_off = reinterpret_cast<const int32_t*>(b + off_dro);
+  L->d_dec_refs = reinterpret_cast<const int32_t*>(b + off_dr);
   return PG_OK;
 }
 
@@ -191,7 +203,8 @@ pg_status pg_layout_info(const pg_layout* L, pg_layout_summary* info) {
   info->max_xcd_cost = 0;
   for (int64_t c : L->xcd_load) info->max_xcd_cost = c > info->max_xcd_cost ? c : info->max_xcd_cost;
   info->num_kv_items = int32_t(L->kv_items.size());
-  info->reserved = 0;
+  info->num_dec_items = int32_t(L->dec_items.size());
+  info->num_dec_refs = int64_t(L->dec_refs.size());
   return PG_OK;
 }
 
@@ -224,6 +237,18 @@ pg_status pg_layout_copy_kv_work(const pg_layout* L, pg_kv_item* items) {
   if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
   if (items && !L->kv_items.empty())
     std::memcpy(items, L->kv_items.data(), sizeof(pg_kv_item) * L->kv_items.size());
+  return PG_OK;
+}
+
+pg_status pg_layout_copy_decode_work(const pg_layout* L, pg_dec_item* items, int32_t* ref_off,
+                                     int32_t* refs) {
+  if (!L) return pg_fail(PG_ERR_INVALID_ARG, "layout is NULL");
+  if (items && !L->dec_items.empty())
+    std::memcpy(items, L->dec_items.data(), sizeof(pg_dec_item) * L->dec_items.size());
+  if (ref_off && !L->dec_ref_off.empty())
+    std::memcpy(ref_off, L->dec_ref_off.data(), 4 * L->dec_ref_off.size());
+  if (refs && !L->dec_refs.empty())
+    std::memcpy(refs, L->dec_refs.data(), 4 * L->dec_refs.size());
   return PG_OK;
 }
 
@@ -296,6 +321,39 @@ pg_status pg_attn_bwd(const pg_layout* L, const void* q, const void* k, const vo
                                     stream);
   pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "backward kernel launch");
+}
+
+pg_status pg_decode_workspace_size(const pg_layout* L, size_t* bytes) {
+  if (!L || !bytes) return pg_fail(PG_ERR_INVALID_ARG, "NULL argument");
+  *bytes = pg_decode_workspace_bytes(*L);
+  return PG_OK;
+}
+
+pg_status pg_attn_decode(const pg_layout* L, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* cur_lens, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, pg_dtype dtype,
+                         float softmax_scale, hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (dtype != PG_BF16 && dtype != PG_F32) return pg_fail(PG_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return pg_fail(PG_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  const int64_t N = int64_t(L->suffix_lens.size());
+  if (N == 0) return PG_OK;
+  if (!q || !o || !lse || !cur_lens) return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (L->T > 0 && (!k_cache || !v_cache)) return pg_fail(PG_ERR_INVALID_ARG, "NULL cache pointer");
+  const bool mfma = dtype == PG_BF16 && L->d == 128;
+  if (mfma) {
+    const size_t need = pg_decode_workspace_bytes(*L);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return pg_fail(PG_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                     workspace ? workspace_bytes : size_t(0), need);
+  }
+  if (N * L->Hq > int64_t(0x7fffffff)) return pg_fail(PG_ERR_INVALID_ARG, "too many query rows");
+  hipError_t e = pg_launch_attn_decode(*L, q, k_cache, v_cache, cur_lens, o, lse, workspace, dtype,
+                                       softmax_scale, stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "decode kernel launch");
 }
 
 pg_status pg_pack_rows(const pg_layout* L, const void* prefix, int32_t prefix_pad,

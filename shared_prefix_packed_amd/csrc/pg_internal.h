@@ -59,6 +59,9 @@ struct pg_layout {
   int64_t max_item_cost = 0;
   std::vector<int64_t> xcd_load;   // summed item cost per XCD queue
   std::vector<pg_kv_item> kv_items;   // backward (dK, dV) work list, launch order
+  std::vector<pg_dec_item> dec_items;   // decode work list, launch order
+  std::vector<int32_t> dec_ref_off;     // [N * Hkv + 1]
+  std::vector<int32_t> dec_refs;        // items holding rows of (response, KV head)
 
   // device copy (one upload slot, filled by pg_layout_upload)
   int device = -1;
@@ -77,6 +80,9 @@ struct pg_layout {
   const int32_t* d_seg_off = nullptr;        // [G+N+1]
   const int32_t* d_suffix_group = nullptr;   // [N]
   const int32_t* d_suffix_lens = nullptr;    // [N]
+  const pg_dec_item* d_dec_items = nullptr;
+  const int32_t* d_dec_ref_off = nullptr;    // [N * Hkv + 1]
+  const int32_t* d_dec_refs = nullptr;
 };
 
 // Host layout builder (pg_layout.cpp). Validates and fills `L`.
@@ -104,6 +110,15 @@ hipError_t pg_launch_pack(const pg_layout& L, const void* prefix, int32_t prefix
 hipError_t pg_launch_unpack(const pg_layout& L, const void* packed, int64_t row_bytes,
                             void* prefix_out, int32_t prefix_pad, void* suffix_out,
                             int32_t suffix_pad, hipStream_t stream);
+hipError_t pg_launch_attn_decode(const pg_layout& L, const void* q, const void* k, const void* v,
+                                 const int32_t* cur_lens, void* o, float* lse, void* workspace,
+                                 pg_dtype dtype, float softmax_scale, hipStream_t stream);
+// Decode step, one workgroup per output row (fp32, or d = 64).
+hipError_t pg_launch_decode_rowwise(const pg_layout& L, const void* q, const void* k,
+                                   const void* v, const int32_t* cur_lens, void* o, float* lse,
+                                   pg_dtype dtype, float softmax_scale, hipStream_t stream);
+// Workspace bytes of the decode kernel for layout L (one partial per item).
+size_t pg_decode_workspace_bytes(const pg_layout& L);
 hipError_t pg_launch_attn_bwd(const pg_layout& L, const void* q, const void* k, const void* v,
                               const void* o, const float* lse, const void* dout, void* dq,
                               void* dk, void* dv, float* delta, float softmax_scale,
@@ -117,3 +132,5 @@ constexpr int PG_ITEM_WAVES = 8;      // waves per work item (workgroup): two pi
 constexpr int PG_KEY_TILE = 64;       // keys per LDS tile
 constexpr int PG_XCDS = 8;            // XCDs of an MI355X; workgroup p runs on XCD p % 8
 constexpr int PG_KV_BLOCK = 128;      // keys per backward dK/dV work item (4 waves x 32)
+constexpr int PG_DEC_CHUNK = 512;     // most cache rows per decode work item
+constexpr int PG_DEC_ROWS = 32;       // most query rows per decode work item (one MFMA column block)

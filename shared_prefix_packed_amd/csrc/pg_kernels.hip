@@ -208,6 +208,67 @@ __global__ __launch_bounds__(64) void attn_rowwise_kernel(
 }
 
 
+// Decode step, one workgroup (one wave) per (response k, query head h): the
+// newest token of response k against its group's prompt rows and its first
+// len_k = clamp(cur_lens[k], 0, capacity_k) own rows (PackInfer abstract,
+// group-contiguous KV cache). Online softmax as in attn_rowwise_kernel. No
+// tables (a layout without tokens): every key set is empty.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_rowwise_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ cur_lens, const int32_t* __restrict__ group_off,
+    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ suffix_group, const int32_t* __restrict__ caps,
+    T* __restrict__ o, float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv,
+    float c_log2) {
+  constexpr int E = D / 64;
+  const int32_t kr = int32_t(blockIdx.x / Hq);
+  const int32_t h = int32_t(blockIdx.x % Hq);
+  const int32_t hk = h / (Hq / Hkv);
+  const int lane = threadIdx.x;
+  float qv[E], acc[E];
+  const T* qr = q + (int64_t(kr) * Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qv[e] = to_f<T>(qr[lane * E + e]);
+    acc[e] = 0.f;
+  }
+  int32_t a = 0, pe = 0, s0 = 0, s1 = 0;
+  if (group_off) {
+    const int32_t g = suffix_group[kr];
+    a = group_off[g];
+    pe = a + prefix_lens[g];
+    s0 = seg_off[g + kr + 1];
+    s1 = s0 + min(max(cur_lens[kr], 0), caps[kr]);
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int32_t j = a; j < s1; ++j) {
+    if (j == pe) j = s0;   // the responses between the prompt and this one
+    if (j >= s1) break;
+    const T* kp = k + (int64_t(j) * Hkv + hk) * D;
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) part += qv[e] * to_f<T>(kp[lane * E + e]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    const float s = part * c_log2;
+    const float mn = fmaxf(m, s);
+    const float alpha = exp2f(m - mn);
+    const float p = exp2f(s - mn);
+    l = l * alpha + p;
+    const T* vp = v + (int64_t(j) * Hkv + hk) * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = acc[e] * alpha + p * to_f<T>(vp[lane * E + e]);
+    m = mn;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  T* orow = o + (int64_t(kr) * Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) orow[lane * E + e] = from_f<T>(acc[e] * inv);
+  if (lane == 0)
+    lse[int64_t(h) * N + kr] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+}
+
 // ------------------------------------------------------- pack and unpack --
 // Row gathers either side of the packed path (verl prefix_grouper_utils.py
 // page, sections 2-3: concatenating each prompt once with its responses, and
@@ -347,6 +408,29 @@ hipError_t pg_launch_attn_rowwise(const pg_layout& L, const void* q, const void*
     if (L.d == 128) PG_ROW(float, 128); else PG_ROW(float, 64);
   }
 #undef PG_ROW
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_decode_rowwise(const pg_layout& L, const void* q, const void* k,
+                                   const void* v, const int32_t* cur_lens, void* o, float* lse,
+                                   pg_dtype dtype, float softmax_scale, hipStream_t stream) {
+  const int32_t N = int32_t(L.suffix_lens.size());
+  const int64_t blocks = int64_t(N) * L.Hq;
+  if (blocks == 0) return hipSuccess;
+  const float c = softmax_scale * 1.44269504088896340736f;
+  const bool have = L.T > 0 && L.d_group_off != nullptr;
+  const int32_t* go = have ? L.d_group_off : nullptr;
+#define PG_DEC(TY, DD)                                                                        \
+  decode_rowwise_kernel<TY, DD><<<dim3(uint32_t(blocks)), dim3(64), 0, stream>>>(           \
+      static_cast<const TY*>(q), static_cast<const TY*>(k), static_cast<const TY*>(v),        \
+      cur_lens, go, L.d_prefix_lens, L.d_seg_off, L.d_suffix_group, L.d_suffix_lens,          \
+      static_cast<TY*>(o), lse, N, L.Hq, L.Hkv, c)
+  if (dtype == PG_BF16) {
+    if (L.d == 128) PG_DEC(uint16_t, 128); else PG_DEC(uint16_t, 64);
+  } else {
+    if (L.d == 128) PG_DEC(float, 128); else PG_DEC(float, 64);
+  }
+#undef PG_DEC
   return hipGetLastError();
 }
 

@@ -311,6 +311,73 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
       for (int32_t i : kpos)
         L.kv_items.push_back(i >= 0 ? kv[size_t(i)] : pg_kv_item{0, 0, 0, 0, 0});
     }
+
+    // Decode work list: every segment of a group that has responses, split
+    // into balanced chunks of at most PG_DEC_CHUNK rows (multiples of 32), per
+    // KV head and per block of at most PG_DEC_ROWS query rows. A prompt chunk
+    // serves the rows of all the group's responses, so each prompt row is read
+    // once per step (plus once per extra row block when n * r > 32); a
+    // response chunk serves its own r rows. Each chunk (with its row blocks) is
+    // one cluster for the XCD placement: its row blocks re-read the same rows.
+    {
+      const int64_t N = int64_t(L.suffix_lens.size());
+      std::vector<pg_dec_item> dec;
+      std::vector<int64_t> dcost, dcluster;
+      std::vector<std::vector<int32_t>> refs(size_t(N * num_kv_heads));
+      int64_t ncl = 0;
+      auto chunked = [&](int32_t a, int32_t b, int32_t resp, int32_t rows0, int32_t nrows) {
+        if (b <= a || nrows <= 0) return;
+        const int32_t len = b - a;
+        const int32_t nch = (len + PG_DEC_CHUNK - 1) / PG_DEC_CHUNK;
+        const int32_t step = ((len + nch - 1) / nch + 31) / 32 * 32;
+        for (int32_t k0 = a; k0 < b; k0 += step) {
+          const int32_t k1 = std::min(b, k0 + step);
+          for (int32_t hk = 0; hk < num_kv_heads; ++hk) {
+            const int64_t cl = ncl++;
+            for (int32_t b0 = 0; b0 < nrows; b0 += PG_DEC_ROWS) {
+              const int32_t row0 = rows0 + b0, nrow = std::min(PG_DEC_ROWS, nrows - b0);
+              const int32_t idx = int32_t(dec.size());
+              dec.push_back(pg_dec_item{k0, k1, hk, resp, a, b, row0, nrow});
+              dcost.push_back(int64_t(k1 - k0) + 64);   // rows read, plus a fixed start-up
+              dcluster.push_back(cl);
+              for (int32_t k = row0 / r; k <= (row0 + nrow - 1) / r; ++k)
+                refs[size_t(int64_t(k) * num_kv_heads + hk)].push_back(idx);
+            }
+          }
+        }
+      };
+      int32_t sg = 0, kresp = 0;
+      for (int32_t g = 0; g < num_groups; ++g) {
+        const int32_t n = suffix_counts[g];
+        if (n > 0) chunked(L.seg_off[sg], L.seg_off[sg + 1], -1, kresp * r, n * r);
+        for (int32_t j = 0; j < n; ++j)
+          chunked(L.seg_off[sg + 1 + j], L.seg_off[sg + 2 + j], kresp + j, (kresp + j) * r, r);
+        sg += 1 + n;
+        kresp += n;
+      }
+      const std::vector<int32_t> dpos = xcd_launch_order(
+          dcost, dcluster, ncl,
+          [&](int32_t a, int32_t b) {
+            const pg_dec_item &ia = dec[size_t(a)], &ib = dec[size_t(b)];
+            if (ia.row0 != ib.row0) return ia.row0 < ib.row0;
+            return ia.k0 < ib.k0;
+          },
+          nullptr);
+      std::vector<int32_t> launch_of(dec.size(), -1);
+      L.dec_items.clear();
+      L.dec_items.reserve(dpos.size());
+      for (size_t p = 0; p < dpos.size(); ++p) {
+        const int32_t i = dpos[p];
+        if (i >= 0) launch_of[size_t(i)] = int32_t(p);
+        L.dec_items.push_back(i >= 0 ? dec[size_t(i)] : pg_dec_item{0, 0, 0, -1, 0, 0, 0, 0});
+      }
+      L.dec_ref_off.assign(size_t(N * num_kv_heads + 1), 0);
+      L.dec_refs.clear();
+      for (size_t u = 0; u < refs.size(); ++u) {
+        for (int32_t i : refs[u]) L.dec_refs.push_back(launch_of[size_t(i)]);
+        L.dec_ref_off[u + 1] = int32_t(L.dec_refs.size());
+      }
+    }
   } catch (const std::bad_alloc&) {
     return pg_fail(PG_ERR_OOM, "host allocation failed");
   }

@@ -323,3 +323,96 @@ def test_pack_and_unpack_argument_errors():
     E = _build([], [])   # no tokens: argument checks still apply
     assert lib.pg_pack_rows(E.handle, None, 0, None, 0, None, 6, None) == -1   # not a multiple of 4
     assert lib.pg_unpack_rows(E.handle, None, 0, None, 0, None, 0, None) == -1
+
+
+# -------------------------------------------------------- decode work list --
+
+def _check_decode_invariants(L, P, S, hq, hkv, d=128):
+    n, flat = _flat(S)
+    lay = O.layout(P, n, flat)
+    T, N, r = int(lay["total_tokens"]), len(flat), hq // hkv
+    group_off = np.asarray(lay["group_off"])
+    items, off, refs = L.decode_work()
+    s = L.summary()
+    assert s.num_dec_items == items.size and s.num_dec_refs == refs.size
+    assert off.size == N * hkv + 1 and off[0] == 0 and off[-1] == refs.size
+    assert L.decode_workspace_size() == items.size * 32 * (d + 2) * 4
+    resp_group = O.response_group(lay)
+    cov = np.zeros((N * r, hkv, T), dtype=np.int64)
+    xcd_of_chunk = {}
+    for p, it in enumerate(items):
+        k0, k1, hk, resp = int(it["k0"]), int(it["k1"]), int(it["hk"]), int(it["resp"])
+        seg0, seg1, row0, nrow = int(it["seg0"]), int(it["seg1"]), int(it["row0"]), int(it["nrow"])
+        if nrow == 0:
+            assert (k0, k1, hk, resp, seg0, seg1, row0) == (0, 0, 0, -1, 0, 0, 0)
+            continue
+        assert 1 <= nrow <= 32 and 0 <= hk < hkv
+        assert seg0 <= k0 < k1 <= seg1 and k1 - k0 <= 512 and (k0 - seg0) % 32 == 0
+        if resp < 0:
+            g = int(np.searchsorted(group_off, seg0, side="right") - 1)
+            assert seg0 == group_off[g] and seg1 == group_off[g] + P[g]
+            members = np.nonzero(resp_group == g)[0]
+            assert members.size > 0
+            assert members[0] * r <= row0 and row0 + nrow <= (members[-1] + 1) * r
+        else:
+            g = int(resp_group[resp])
+            assert seg0 == int(lay["seg_off"][g + resp + 1]) and seg1 - seg0 == flat[resp]
+            assert resp * r <= row0 and row0 + nrow <= (resp + 1) * r
+        cov[row0:row0 + nrow, hk, k0:k1] += 1
+        assert xcd_of_chunk.setdefault((k0, k1, hk), p % 8) == p % 8, "row blocks split over XCDs"
+    caps = np.asarray(flat, dtype=np.int64)
+    for k in range(N):
+        want = np.zeros(T, dtype=np.int64)
+        want[O.decode_key_rows(lay, caps, k)] = 1
+        for i in range(r):
+            for hk in range(hkv):
+                assert np.array_equal(cov[k * r + i, hk], want), (k, i, hk)
+        for hk in range(hkv):
+            got = set(refs[off[k * hkv + hk]:off[k * hkv + hk + 1]].tolist())
+            exp = {p for p, it in enumerate(items) if it["nrow"] > 0 and it["hk"] == hk
+                   and it["row0"] < (k + 1) * r and it["row0"] + it["nrow"] > k * r}
+            assert got == exp, (k, hk)
+    assert items.size == 0 or items[-1]["nrow"] > 0, "no trailing padding"
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("heads", [(4, 1), (32, 8), (6, 2), (64, 1), (3, 3)])
+def test_decode_work_list_invariants(shape, heads):
+    P, S = shape
+    L = _build(P, S, hq=heads[0], hkv=heads[1])
+    _check_decode_invariants(L, P, S, *heads)
+
+
+def test_decode_work_list_on_long_segments():
+    # a 1500-row prompt (balanced chunks of at most 512 rows) with 10 responses
+    # of 4 query heads each (40 rows: two row blocks per prompt chunk)
+    P, S = [1500], [[700, 3, 0, 64, 65, 1, 2, 3, 4, 513]]
+    L = _build(P, S, hq=8, hkv=2)
+    _check_decode_invariants(L, P, S, 8, 2)
+    items, _, _ = L.decode_work()
+    prompt = items[(items["resp"] == -1) & (items["nrow"] > 0)]
+    assert sorted(set((prompt["k1"] - prompt["k0"]).tolist())) == [476, 512]
+
+
+def test_decode_work_list_on_dpo_workload():
+    w = make_workload(1)
+    L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens, 32, 8, 128, 5e5)
+    _check_decode_invariants(L, w.prefix_lens.tolist(), [s for _, s in w.groups()], 32, 8)
+
+
+def test_decode_argument_errors():
+    lib = _lib.load()
+    L = _build([5], [[3]])
+    dummy = ctypes.c_void_p(16)
+    f = ctypes.c_float
+    args = lambda scale: [dummy] * 7 + [ctypes.c_size_t(1 << 20), 1, f(scale), None]
+    assert lib.pg_attn_decode(L.handle, *args(0.1)) == -5          # not uploaded
+    assert lib.pg_attn_decode(None, *args(0.1)) == -1
+    E = _build([0, 0], [[0], []])        # no tokens, one response: argument checks still apply
+    assert lib.pg_attn_decode(E.handle, *args(0.0)) == -1           # scale
+    assert lib.pg_attn_decode(E.handle, None, None, None, None, None, None, None,
+                              ctypes.c_size_t(0), 1, f(0.1), None) == -1   # NULL tensors
+    assert lib.pg_attn_decode(E.handle, *([dummy] * 7), ctypes.c_size_t(0), 7, f(0.1), None) == -1
+    n = ctypes.c_size_t(123)
+    assert lib.pg_decode_workspace_size(E.handle, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.pg_decode_workspace_size(None, ctypes.byref(n)) == -1
