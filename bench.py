@@ -119,6 +119,7 @@ def main(argv=None):
     ap.add_argument("--no-unpacked", action="store_true", help="skip the unpacked-layout baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip timing pg_attn_bwd")
     ap.add_argument("--no-gathers", action="store_true", help="skip timing pg_pack_rows / pg_unpack_rows")
+    ap.add_argument("--no-decode", action="store_true", help="skip timing pg_attn_decode")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against a known byte count)")
@@ -141,8 +142,8 @@ def main(argv=None):
         print(json.dumps({"copy_bytes": 4 * n, "launches": 5}), flush=True)
         return 0
     import shared_prefix_packed_amd as pg
-    from shared_prefix_packed_amd.baseline import unpacked_workload
-    from workloads import draw_qkv, draw_tensor, make_workload, sha256
+    from shared_prefix_packed_amd.baseline import unpacked_decode_workload, unpacked_workload
+    from workloads import draw_decode, draw_qkv, draw_tensor, make_workload, sha256
 
     pg.load()   # fails loudly without the built library
     w = make_workload(args.workload)
@@ -317,6 +318,68 @@ def main(argv=None):
         L.close()
         del pre, suf, packed, outs, cpy
 
+    # one decode step with this batch's layout taken as the KV cache (response
+    # segments at capacity, current lengths drawn in [1, capacity])
+    decode = None
+    if not args.no_decode and w.dtype == "bf16" and d == 128 and len(w.suffix_lens) > 0:
+        dx = draw_decode(w)
+        L = build()
+        qd = dev(dx["q"])
+        cur_np = dx["cur_lens"].astype(np.int64)
+        cur = torch.from_numpy(dx["cur_lens"]).cuda()
+        Nr = qd.shape[0]
+        od = torch.empty_like(qd)
+        ld = torch.empty((Hq, Nr), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, L.decode_workspace_size()), dtype=torch.uint8, device="cuda")
+
+        def time_decode(layout, kc, vc, work):
+            for _ in range(3):
+                pg.pg_attn_decode(layout, qd, kc, vc, cur, w.softmax_scale, o=od, lse=ld,
+                                  workspace=work, stream=stream)
+            ts = []
+            for _ in range(20):
+                a_, b_ = ev(), ev()
+                a_.record(stream)
+                pg.pg_attn_decode(layout, qd, kc, vc, cur, w.softmax_scale, o=od, lse=ld,
+                                  workspace=work, stream=stream)
+                b_.record(stream)
+                ts.append((a_, b_))
+            torch.cuda.synchronize()
+            return float(np.mean([a_.elapsed_time(b_) for a_, b_ in ts]))
+
+        dec_ms = time_decode(L, kr, v, ws)
+        # algorithmic bytes: each group's prompt K/V once (groups with
+        # responses), each response's valid K/V rows once, Q read, O and lse written
+        row_kv = Hkv * d * 2 * 2
+        has_resp = np.asarray(w.suffix_counts) > 0
+        prompt_rows = int(np.asarray(w.prefix_lens, dtype=np.int64)[has_resp].sum())
+        valid_rows = int(np.clip(cur_np, 0, np.asarray(w.suffix_lens, dtype=np.int64)).sum())
+        qo_bytes = 2 * Nr * Hq * d * 2 + Hq * Nr * 4
+        dec_bytes = (prompt_rows + valid_rows) * row_kv + qo_bytes
+        resp_prompt = np.repeat(np.asarray(w.prefix_lens, dtype=np.int64), w.suffix_counts)
+        unpacked_bytes = int(resp_prompt.sum() + valid_rows) * row_kv + qo_bytes
+        decode = {"ms": round(dec_ms, 4), "bytes": dec_bytes,
+                  "gbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                  "pct_of_hbm_peak": round(100 * dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                  "responses": Nr, "work_items": L.summary().num_dec_items,
+                  "bytes_unpacked": unpacked_bytes,
+                  "bytes_definition": "K and V rows read once (each group's prompt once, each "
+                                      "response's valid rows once), Q read, O and lse written"}
+        L.close()
+        if not args.no_unpacked:
+            un = unpacked_decode_workload(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+            idx = torch.from_numpy(un.gather).cuda()
+            ku, vu = kr[idx].contiguous(), v[idx].contiguous()
+            Lu = pg.pg_build_layout(un.prefix_lens, un.suffix_counts, un.suffix_lens, Hq, Hkv, d,
+                                    w.rope_theta, stream=stream)
+            wsu = torch.empty(max(1, Lu.decode_workspace_size()), dtype=torch.uint8, device="cuda")
+            un_ms = time_decode(Lu, ku, vu, wsu)
+            decode["unpacked_ms"] = round(un_ms, 4)
+            decode["speedup_vs_unpacked"] = round(un_ms / dec_ms, 3)
+            Lu.close()
+            del ku, vu, wsu
+        del qd, od, ld, ws
+
     traffic = load_traffic(w.name)
     roof = {
         "bound": "mfma",
@@ -372,6 +435,7 @@ def main(argv=None):
         "roofline": roof,
         "backward": bwd,
         "gathers": gathers,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -23,7 +23,8 @@
 //    and the row sum go to the workspace as the item's partial result.
 //  * decode_merge_kernel: one wave per (response, query head) combines the
 //    partials of the items holding its row (O = sum e^(m_i - M) O_i / sum
-//    e^(m_i - M) l_i) and writes O (bf16) and lse.
+//    e^(m_i - M) l_i) and writes O (bf16) and lse; the partials are fetched
+//    side by side, one lane each, rather than one after another.
 #include "pg_hip_common.h"
 #include "pg_internal.h"
 
@@ -204,7 +205,11 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecArgs a) {
   }
 }
 
-// One wave per output row (response k, query head h): 2 values of d per lane.
+// One wave per output row (response k, query head h). The lanes first take
+// up to 64 of the row's partials at once (merge-list entry, item, then its
+// (m, l): three dependent loads for all of them together), the wave reduces
+// the common max M and the weights e^(m_i - M); then every lane sums its 2
+// values of d over the partials, eight row loads in flight at a time.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
     const pg_dec_item* __restrict__ items, const int32_t* __restrict__ ref_off,
@@ -217,22 +222,57 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int hk = h / r;
   const int qrow = k * r + (h - hk * r);
   float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
-  if (ref_off) {
-    const int j1 = ref_off[int64_t(k) * Hkv + hk + 1];
-    for (int j = ref_off[int64_t(k) * Hkv + hk]; j < j1; ++j) {
-      const int idx = refs[j];
+  const int j0 = ref_off ? ref_off[int64_t(k) * Hkv + hk] : 0;
+  const int j1 = ref_off ? ref_off[int64_t(k) * Hkv + hk + 1] : 0;
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int nb = min(64, j1 - jb);
+    // lane j: partial jb + j (slot 0 of item 0 stands in for lanes without one)
+    int slot = 0;   // items * 32 fits in 32 bits (T < 2^30 rows)
+    float m = -INFINITY, l = 0.f;
+    if (lane < nb) {
+      const int idx = refs[jb + lane];
       const int row0 = items[idx].row0, nrow = items[idx].nrow;
-      if (qrow < row0 || qrow >= row0 + nrow) continue;
-      const int64_t slot = int64_t(idx) * PG_DEC_ROWS + (qrow - row0);
-      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * slot);
-      if (!(ml.y > 0.f)) continue;   // no key of this item is valid
-      const float2 ov = *reinterpret_cast<const float2*>(ws_o + slot * D + 2 * lane);
-      const float mn = fmaxf(M, ml.x);
-      const float a0 = exp2f(M - mn), a1 = exp2f(ml.x - mn);
-      acc0 = acc0 * a0 + ov.x * a1;
-      acc1 = acc1 * a0 + ov.y * a1;
-      L = L * a0 + ml.y * a1;
-      M = mn;
+      if (qrow >= row0 && qrow < row0 + nrow) {
+        slot = idx * PG_DEC_ROWS + (qrow - row0);
+        const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * int64_t(slot));
+        if (ml.y > 0.f) {   // else no key of the item is valid for this row
+          m = ml.x;
+          l = ml.y;
+        }
+      }
+    }
+    float mb = m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off, 64));
+    if (mb == -INFINITY) continue;
+    const float mn = fmaxf(M, mb);
+    const float a0 = exp2f(M - mn);
+    const float wgt = l > 0.f ? exp2f(m - mn) : 0.f;
+    float lb = wgt * l;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lb += __shfl_xor(lb, off, 64);
+    L = L * a0 + lb;
+    acc0 *= a0;
+    acc1 *= a0;
+    M = mn;
+    for (int j = 0; j < nb; j += 8) {
+      float2 ov[8];
+      float wj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int src = min(j + u, nb - 1);   // wave-uniform
+        const float wsrc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), src));
+        wj[u] = j + u < nb ? wsrc : 0.f;
+        const int64_t sl = __builtin_amdgcn_readlane(slot, src);
+        ov[u] = *reinterpret_cast<const float2*>(ws_o + sl * D + 2 * lane);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (wj[u] != 0.f) {   // skip weight-0 partials: their O rows may hold anything
+          acc0 = fmaf(wj[u], ov[u].x, acc0);
+          acc1 = fmaf(wj[u], ov[u].y, acc1);
+        }
+      }
     }
   }
   const bool any = L > 0.f;

@@ -60,6 +60,7 @@ struct pg_layout {
   std::vector<int64_t> xcd_load;   // summed item cost per XCD queue
   std::vector<pg_kv_item> kv_items;   // backward (dK, dV) work list, launch order
   std::vector<pg_dec_item> dec_items;   // decode work list, launch order
+  int32_t dec_chunk = 0;                // rows per decode chunk (at most)
   std::vector<int32_t> dec_ref_off;     // [N * Hkv + 1]
   std::vector<int32_t> dec_refs;        // items holding rows of (response, KV head)
 
@@ -133,4 +134,5 @@ constexpr int PG_KEY_TILE = 64;       // keys per LDS tile
 constexpr int PG_XCDS = 8;            // XCDs of an MI355X; workgroup p runs on XCD p % 8
 constexpr int PG_KV_BLOCK = 128;      // keys per backward dK/dV work item (4 waves x 32)
 constexpr int PG_DEC_CHUNK = 512;     // most cache rows per decode work item
+constexpr int PG_DEC_TARGET = 1024;   // decode work items aimed at per step
 constexpr int PG_DEC_ROWS = 32;       // most query rows per decode work item (one MFMA column block)

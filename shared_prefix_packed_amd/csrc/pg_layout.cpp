@@ -313,8 +313,10 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
     }
 
     // Decode work list: every segment of a group that has responses, split
-    // into balanced chunks of at most PG_DEC_CHUNK rows (multiples of 32), per
-    // KV head and per block of at most PG_DEC_ROWS query rows. A prompt chunk
+    // into balanced chunks (multiples of 32 rows) per KV head and per block of
+    // at most PG_DEC_ROWS query rows. The chunk length aims at about
+    // PG_DEC_TARGET items for the whole step (several waves per CU on small
+    // batches), between 64 and PG_DEC_CHUNK rows. A prompt chunk
     // serves the rows of all the group's responses, so each prompt row is read
     // once per step (plus once per extra row block when n * r > 32); a
     // response chunk serves its own r rows. Each chunk (with its row blocks) is
@@ -325,10 +327,23 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
       std::vector<int64_t> dcost, dcluster;
       std::vector<std::vector<int32_t>> refs(size_t(N * num_kv_heads));
       int64_t ncl = 0;
+      int64_t dec_rows = 0;   // cache rows a step may read, summed over KV heads
+      {
+        int32_t sg = 0;
+        for (int32_t g = 0; g < num_groups; ++g) {
+          const int32_t n = suffix_counts[g];
+          if (n > 0) dec_rows += int64_t(L.seg_off[sg + 1 + n] - L.seg_off[sg]) * num_kv_heads;
+          sg += 1 + n;
+        }
+      }
+      const int64_t per_item = (dec_rows + PG_DEC_TARGET - 1) / PG_DEC_TARGET;
+      const int32_t chunk =
+          int32_t(std::min<int64_t>(PG_DEC_CHUNK, std::max<int64_t>(64, (per_item + 31) / 32 * 32)));
+      L.dec_chunk = chunk;
       auto chunked = [&](int32_t a, int32_t b, int32_t resp, int32_t rows0, int32_t nrows) {
         if (b <= a || nrows <= 0) return;
         const int32_t len = b - a;
-        const int32_t nch = (len + PG_DEC_CHUNK - 1) / PG_DEC_CHUNK;
+        const int32_t nch = (len + chunk - 1) / chunk;
         const int32_t step = ((len + nch - 1) / nch + 31) / 32 * 32;
         for (int32_t k0 = a; k0 < b; k0 += step) {
           const int32_t k1 = std::min(b, k0 + step);
