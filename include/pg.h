@@ -235,7 +235,9 @@ pg_status pg_position_ids(const pg_layout* layout, int64_t* pos, hipStream_t str
  *  pos           device int64 [T], any values >= 0 (normally pg_position_ids)
  *  q_in, q_out   device [T, Hq, d];  k_in, k_out  device [T, Hkv, d]
  *                q_out may equal q_in and k_out may equal k_in (in place);
- *                other overlaps are not allowed.
+ *                other overlaps are not allowed. One pair may be NULL as a whole
+ *                (q_in and q_out, or k_in and k_out): only the other is rotated
+ *                (a decode step rotates the new token's K and Q separately).
  *  dtype         PG_F32 or PG_BF16
  */
 pg_status pg_rope(const pg_layout* layout, const int64_t* pos, const void* q_in,
@@ -262,6 +264,7 @@ pg_status pg_rope(const pg_layout* layout, const int64_t* pos, const void* q_in,
 pg_status pg_attn_fwd(const pg_layout* layout, const void* q, const void* k, const void* v,
                       void* o, float* lse, pg_dtype dtype, float softmax_scale,
                       hipStream_t stream);
+
 
 /*
  * pg_pack_rows -- build packed rows from right-padded per-prompt and

@@ -202,22 +202,31 @@ def pg_position_ids(layout: Layout, pos=None, stream=None):
 
 def pg_rope(layout: Layout, pos, q, k, q_out=None, k_out=None, stream=None):
     """RoPE of q [T, Hq, d] and k [T, Hkv, d] at `pos`; out-of-place unless
-    q_out is q / k_out is k."""
+    q_out is q / k_out is k. q or k may be None: only the other is rotated
+    (the returned output for the missing one is None)."""
     import torch
     T, Hq, Hkv, d = layout.total_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    if q is None and k is None:
+        raise ValueError("nothing to rotate")
     _check_tensor("pos", pos, (T,), torch.int64)
-    _check_tensor("q", q, (T, Hq, d))
-    _check_tensor("k", k, (T, Hkv, d), q.dtype)
-    if q_out is None:
-        q_out = torch.empty_like(q)
-    if k_out is None:
-        k_out = torch.empty_like(k)
-    _check_tensor("q_out", q_out, (T, Hq, d), q.dtype)
-    _check_tensor("k_out", k_out, (T, Hkv, d), q.dtype)
-    check(load().pg_rope(layout.handle, ctypes.c_void_p(pos.data_ptr()),
-                         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-                         ctypes.c_void_p(q_out.data_ptr()), ctypes.c_void_p(k_out.data_ptr()),
-                         _dtype_code(q), _stream_handle(stream)), "pg_rope")
+    ref = q if q is not None else k
+    if q is not None:
+        _check_tensor("q", q, (T, Hq, d))
+        if q_out is None:
+            q_out = torch.empty_like(q)
+        _check_tensor("q_out", q_out, (T, Hq, d), ref.dtype)
+    else:
+        q_out = None
+    if k is not None:
+        _check_tensor("k", k, (T, Hkv, d), ref.dtype)
+        if k_out is None:
+            k_out = torch.empty_like(k)
+        _check_tensor("k_out", k_out, (T, Hkv, d), ref.dtype)
+    else:
+        k_out = None
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else None)
+    check(load().pg_rope(layout.handle, ptr(pos), ptr(q), ptr(k), ptr(q_out), ptr(k_out),
+                         _dtype_code(ref), _stream_handle(stream)), "pg_rope")
     return q_out, k_out
 
 

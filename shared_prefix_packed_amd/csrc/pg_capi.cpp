@@ -275,8 +275,8 @@ pg_status pg_rope(const pg_layout* L, const int64_t* pos, const void* q_in, cons
   if (dtype != PG_F32 && dtype != PG_BF16)
     return pg_fail(PG_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
   if (L->T == 0) return PG_OK;
-  if (!pos || !q_in || !k_in || !q_out || !k_out)
-    return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!pos || (!q_in != !q_out) || (!k_in != !k_out) || (!q_in && !k_in))
+    return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer (a pair may be skipped only whole)");
   hipError_t e = pg_launch_rope(*L, pos, q_in, k_in, q_out, k_out, dtype, stream);
   pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "rope kernel launch");

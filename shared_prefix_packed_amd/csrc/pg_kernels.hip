@@ -7,9 +7,14 @@
 // packed key set of every token directly (fp32, and bf16 with d = 64).
 #include <hip/hip_runtime.h>
 
+#include "pg_hip_common.h"
 #include "pg_internal.h"
 
 namespace {
+
+using pg_hip::f64_to_bf16_bits;
+using pg_hip::rope_hi;
+using pg_hip::rope_lo;
 
 // ------------------------------------------------------------- positions --
 // One thread per token: pos = t - g0 in the prefix, P + (t - ss) in a suffix.
@@ -30,22 +35,6 @@ __global__ __launch_bounds__(256) void positions_kernel(const int32_t* __restric
 // rotation runs in fp64 and is rounded once to the storage dtype: in fp32,
 // x cos - y sin loses to cancellation near zero more than a bf16 ulp there.
 constexpr int ROPE_TOK = 4;
-
-// fp64 -> bf16 bits, nearest-even, in one rounding (no detour through fp32).
-__device__ inline uint32_t f64_to_bf16_bits(double x) {
-  const uint64_t u = uint64_t(__double_as_longlong(x));
-  const uint64_t mag = u & 0x7fffffffffffffffull;
-  const uint32_t sign = uint32_t(u >> 48) & 0x8000u;
-  if (mag < 0x3810000000000000ull) {   // |x| < 2^-126: below bf16 normals
-    const uint32_t f = __float_as_uint(float(x));   // tiny values go through fp32
-    return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16;
-  }
-  // keep 7 mantissa bits: round at bit 45 of the fp64 pattern, ties to even
-  const uint64_t r = (mag + ((uint64_t(1) << 44) - 1) + ((mag >> 45) & 1)) >> 45;   // exp11|mant7
-  const uint32_t e = uint32_t(r >> 7);                                                // fp64 exponent
-  if (e >= 1023 + 128) return sign | 0x7f80u;                                         // overflow: inf
-  return sign | ((e - 1023 + 127) << 7) | uint32_t(r & 0x7f);
-}
 
 template <typename T>
 struct Vec8;
@@ -113,9 +102,11 @@ __global__ __launch_bounds__(256) void rope_kernel(const int64_t* __restrict__ p
     const T* src;
     T* dst;
     if (hh < Hq) {
+      if (!q_in) continue;   // K only
       src = q_in + (t * Hq + hh) * D;
       dst = q_out + (t * Hq + hh) * D;
     } else {
+      if (!k_in) continue;   // Q only
       src = k_in + (t * Hkv + (hh - Hq)) * D;
       dst = k_out + (t * Hkv + (hh - Hq)) * D;
     }
@@ -130,8 +121,8 @@ __global__ __launch_bounds__(256) void rope_kernel(const int64_t* __restrict__ p
         const int e = 2 * m + e2;
         const double c = cs[tt][ch * 8 + e], s = sn[tt][ch * 8 + e];
         const double xl = lo.get(e), xh = hi.get(e);
-        rl[e2] = xl * c - xh * s;
-        rh[e2] = xh * c + xl * s;
+        rl[e2] = rope_lo(xl, xh, c, s);
+        rh[e2] = rope_hi(xl, xh, c, s);
       }
       ylo.set2(m, rl[0], rl[1]);
       yhi.set2(m, rh[0], rh[1]);

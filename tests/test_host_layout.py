@@ -425,3 +425,15 @@ def test_decode_argument_errors():
     n = ctypes.c_size_t(123)
     assert lib.pg_decode_workspace_size(E.handle, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.pg_decode_workspace_size(None, ctypes.byref(n)) == -1
+
+
+def test_single_pair_rope_argument_errors():
+    lib = _lib.load()
+    dummy = ctypes.c_void_p(16)
+    L = _build([5], [[3]])
+    assert lib.pg_rope(L.handle, dummy, None, dummy, None, dummy, 1, None) == -5   # not uploaded
+    E = _build([0, 0], [[0], []])   # no tokens: a no-op whatever is passed
+    assert lib.pg_rope(E.handle, dummy, None, dummy, None, dummy, 1, None) == 0
+    lay = pg.pg_build_layout_host([5], [1], [3], 4, 1, 128, 1e4)
+    # argument checks need a device copy; they are exercised on the GPU
+    assert lib.pg_rope(lay.handle, dummy, None, None, None, None, 1, None) == -5
