@@ -550,6 +550,64 @@ def unpack_rows(packed: np.ndarray, lay, prefix_pad: int, suffix_pad: int):
     return pre, suf
 
 
+# ------------------------------------------------------- padded form --
+
+
+def group_lens(lay) -> np.ndarray:
+    """Tokens of every group's packed row (prefix plus all its responses)."""
+    return np.diff(np.asarray(lay["group_off"], dtype=np.int64))
+
+
+def padded_positions(lay, max_len: int) -> np.ndarray:
+    """Position ids of the right-padded form [G, max_len].
+
+    verl page, section 1 (building position ids): a zero-filled int64 tensor;
+    row g holds its prompt's positions 0..P-1, then every non-empty response's
+    P..P+S-1 in order; padding stays 0. Written out by that loop.
+    Pinned by: hand-derived rows of the tiny workload; real tokens equal
+    ``positions`` (the packed form).
+    """
+    G = len(lay["prefix_lens"])
+    out = np.zeros((G, max_len), dtype=np.int64)
+    k = 0
+    for g in range(G):
+        P = int(lay["prefix_lens"][g])
+        out[g, :P] = np.arange(P)
+        cur = P
+        for _ in range(int(lay["suffix_counts"][g])):
+            S = int(lay["suffix_lens"][k])
+            k += 1
+            if S > 0:
+                out[g, cur:cur + S] = np.arange(P, P + S)
+                cur += S
+    return out
+
+
+def padding_mask(lay, max_len: int) -> np.ndarray:
+    """1 on the real tokens of each padded row, 0 on right padding (uint8)."""
+    n = group_lens(lay)
+    return (np.arange(max_len)[None, :] < n[:, None]).astype(np.uint8)
+
+
+def pad_rows(packed: np.ndarray, lay, max_len: int) -> np.ndarray:
+    """Packed rows [T, ...] to the right-padded form [G, max_len, ...]: row g
+    is its group's packed row, then zeros."""
+    G = len(lay["prefix_lens"])
+    out = np.zeros((G, max_len) + packed.shape[1:], dtype=packed.dtype)
+    for g in range(G):
+        a, b = int(lay["group_off"][g]), int(lay["group_off"][g + 1])
+        out[g, :b - a] = packed[a:b]
+    return out
+
+
+def unpad_rows(padded: np.ndarray, lay) -> np.ndarray:
+    """The right-padded form [G, max_len, ...] back to packed rows [T, ...]."""
+    parts = [padded[g, :int(n)] for g, n in enumerate(group_lens(lay))]
+    if not parts:
+        return np.zeros((0,) + padded.shape[2:], dtype=padded.dtype)
+    return np.concatenate(parts, axis=0)
+
+
 # ------------------------------------------------------------------ decode --
 
 
