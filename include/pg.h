@@ -73,6 +73,9 @@ typedef struct pg_layout_summary {
   int32_t num_kv_items;    /* work items of the backward dK/dV launch            */
   int32_t num_dec_items;   /* work items of the decode launch (padding included) */
   int64_t num_dec_refs;    /* entries of the decode merge lists                  */
+  int32_t max_group_len;   /* longest group row (prefix + its responses): the
+                              smallest max_len of the padded form                */
+  int32_t reserved;        /* 0                                                  */
 } pg_layout_summary;
 
 /* One work item of the attention launch: query tokens [t0, t1) of one group,
@@ -361,6 +364,30 @@ pg_status pg_attn_decode(const pg_layout* layout, const void* q, const void* k_c
                          const void* v_cache, const int32_t* cur_lens, void* o, float* lse,
                          void* workspace, size_t workspace_bytes, pg_dtype dtype,
                          float softmax_scale, hipStream_t stream);
+
+/*
+ * Right-padded compatibility form. The verl page (sections 1-2) keeps a batch
+ * as [G, max_len]: row g is group g's packed row (prompt, then each response),
+ * right-padded; its position ids start from zeros (section 1), so padding
+ * keeps position 0, and its padding mask marks the real tokens. These calls
+ * convert between that form and the packed rows every other call takes.
+ * max_len must be >= max_group_len (pg_layout_info); PG_ERR_INVALID_ARG
+ * otherwise, or for NULL outputs or a row_bytes that is not a positive
+ * multiple of 4. Device pointers; outputs are written completely.
+ */
+
+/* pos: int64 [G, max_len], the padded form's position ids (padding 0);
+ * mask: uint8 [G, max_len] or NULL, 1 on real tokens and 0 on padding. */
+pg_status pg_position_ids_padded(const pg_layout* layout, int32_t max_len, int64_t* pos,
+                                 uint8_t* mask, hipStream_t stream);
+
+/* padded [G, max_len] rows of row_bytes <- packed [T] rows; padding rows zero. */
+pg_status pg_pad_rows(const pg_layout* layout, const void* packed, int64_t row_bytes,
+                      void* padded, int32_t max_len, hipStream_t stream);
+
+/* packed [T] rows <- the real rows of padded [G, max_len] (padding not read). */
+pg_status pg_unpad_rows(const pg_layout* layout, const void* padded, int32_t max_len,
+                        int64_t row_bytes, void* packed, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* pg_status_string(pg_status status);

@@ -13,8 +13,11 @@ from .api import (  # noqa: F401
     pg_build_layout_host,
     pg_layout_upload,
     pg_pack_rows,
+    pg_pad_rows,
+    pg_position_ids_padded,
     pg_position_ids,
     pg_rope,
     pg_unpack_rows,
+    pg_unpad_rows,
 )
 from ._lib import PgError, load  # noqa: F401

@@ -38,6 +38,8 @@ class LayoutSummary(ctypes.Structure):
         ("num_kv_items", c_int32),
         ("num_dec_items", c_int32),
         ("num_dec_refs", ctypes.c_int64),
+        ("max_group_len", c_int32),
+        ("reserved", c_int32),
     ]
 
 
@@ -91,6 +93,9 @@ SIGNATURES = {
                                ctypes.c_int64, c_void_p]),
     "pg_unpack_rows": (c_int32, [c_void_p, c_void_p, ctypes.c_int64, c_void_p, c_int32,
                                  c_void_p, c_int32, c_void_p]),
+    "pg_position_ids_padded": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    "pg_pad_rows": (c_int32, [c_void_p, c_void_p, ctypes.c_int64, c_void_p, c_int32, c_void_p]),
+    "pg_unpad_rows": (c_int32, [c_void_p, c_void_p, c_int32, ctypes.c_int64, c_void_p, c_void_p]),
     "pg_status_string": (ctypes.c_char_p, [c_int32]),
     "pg_last_error": (ctypes.c_char_p, []),
 }

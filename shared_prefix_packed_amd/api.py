@@ -362,3 +362,58 @@ def pg_unpack_rows(layout: Layout, packed, prefix_pad: int, suffix_pad: int, str
                                 _stream_handle(stream)),
           "pg_unpack_rows")
     return pre, suf
+
+
+# ------------------------------------------------- right-padded form --
+
+def _max_len(layout: Layout, max_len) -> int:
+    return layout.summary().max_group_len if max_len is None else int(max_len)
+
+
+def pg_position_ids_padded(layout: Layout, max_len: Optional[int] = None, stream=None):
+    """Position ids (int64) and padding mask (uint8) of the right-padded form
+    [G, max_len]; max_len defaults to the longest group row."""
+    import torch
+    G, L = layout.summary().num_groups, _max_len(layout, max_len)
+    pos = torch.empty((G, L), dtype=torch.int64, device="cuda")
+    mask = torch.empty((G, L), dtype=torch.uint8, device="cuda")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() else None)
+    check(load().pg_position_ids_padded(layout.handle, L, ptr(pos), ptr(mask),
+                                        _stream_handle(stream)), "pg_position_ids_padded")
+    return pos, mask
+
+
+def pg_pad_rows(layout: Layout, packed, max_len: Optional[int] = None, padded=None, stream=None):
+    """Packed rows [T, ...] to the right-padded form [G, max_len, ...]
+    (max_len: that of ``padded`` if given, else the longest group row)."""
+    import torch
+    if max_len is None and padded is not None and padded.dim() >= 2:
+        max_len = padded.shape[1]
+    G, L = layout.summary().num_groups, _max_len(layout, max_len)
+    _check_tensor("packed", packed, (layout.total_tokens,) + tuple(packed.shape[1:]))
+    rb = _row_bytes(packed, 1)
+    if padded is None:
+        padded = torch.empty((G, L) + tuple(packed.shape[1:]), dtype=packed.dtype, device="cuda")
+    _check_tensor("padded", padded, (G, L) + tuple(packed.shape[1:]), packed.dtype)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() else None)
+    check(load().pg_pad_rows(layout.handle, ptr(packed), ctypes.c_int64(rb), ptr(padded), L,
+                             _stream_handle(stream)), "pg_pad_rows")
+    return padded
+
+
+def pg_unpad_rows(layout: Layout, padded, packed=None, stream=None):
+    """The right-padded form [G, max_len, ...] back to packed rows [T, ...]."""
+    import torch
+    G, T = layout.summary().num_groups, layout.total_tokens
+    if padded.dim() < 2 or padded.shape[0] != G:
+        raise ValueError(f"padded must be [G={G}, max_len, ...], got {tuple(padded.shape)}")
+    L = padded.shape[1]
+    tail = tuple(padded.shape[2:])
+    if packed is None:
+        packed = torch.empty((T,) + tail, dtype=padded.dtype, device="cuda")
+    _check_tensor("packed", packed, (T,) + tail, padded.dtype)
+    rb = _row_bytes(packed, 1)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() else None)
+    check(load().pg_unpad_rows(layout.handle, ptr(padded), L, ctypes.c_int64(rb), ptr(packed),
+                               _stream_handle(stream)), "pg_unpad_rows")
+    return packed

@@ -205,6 +205,8 @@ pg_status pg_layout_info(const pg_layout* L, pg_layout_summary* info) {
   info->num_kv_items = int32_t(L->kv_items.size());
   info->num_dec_items = int32_t(L->dec_items.size());
   info->num_dec_refs = int64_t(L->dec_refs.size());
+  info->max_group_len = L->max_group_len;
+  info->reserved = 0;
   return PG_OK;
 }
 
@@ -354,6 +356,60 @@ pg_status pg_attn_decode(const pg_layout* L, const void* q, const void* k_cache,
                                        softmax_scale, stream);
   pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "decode kernel launch");
+}
+
+namespace {
+pg_status check_padded(const pg_layout* L, int32_t max_len) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (max_len < L->max_group_len)
+    return pg_fail(PG_ERR_INVALID_ARG, "max_len %d shorter than the longest group row %d", max_len,
+                   L->max_group_len);
+  return PG_OK;
+}
+pg_status check_row_bytes(int64_t row_bytes) {
+  if (row_bytes <= 0 || row_bytes % 4 != 0)
+    return pg_fail(PG_ERR_INVALID_ARG, "row_bytes %lld must be a positive multiple of 4",
+                   (long long)row_bytes);
+  return PG_OK;
+}
+}  // namespace
+
+pg_status pg_position_ids_padded(const pg_layout* L, int32_t max_len, int64_t* pos, uint8_t* mask,
+                                 hipStream_t stream) {
+  pg_status s = check_padded(L, max_len);
+  if (s != PG_OK) return s;
+  const int64_t G = int64_t(L->group_off.size()) - 1;
+  if (G * max_len == 0) return PG_OK;
+  if (!pos) return pg_fail(PG_ERR_INVALID_ARG, "pos is NULL");
+  hipError_t e = pg_launch_positions_padded(*L, max_len, pos, mask, stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "padded positions kernel launch");
+}
+
+pg_status pg_pad_rows(const pg_layout* L, const void* packed, int64_t row_bytes, void* padded,
+                      int32_t max_len, hipStream_t stream) {
+  pg_status s = check_padded(L, max_len);
+  if (s == PG_OK) s = check_row_bytes(row_bytes);
+  if (s != PG_OK) return s;
+  const int64_t G = int64_t(L->group_off.size()) - 1;
+  if (G * max_len == 0) return PG_OK;
+  if (!padded || (L->T > 0 && !packed)) return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e = pg_launch_pad(*L, packed, row_bytes, padded, max_len, stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "pad kernel launch");
+}
+
+pg_status pg_unpad_rows(const pg_layout* L, const void* padded, int32_t max_len, int64_t row_bytes,
+                        void* packed, hipStream_t stream) {
+  pg_status s = check_padded(L, max_len);
+  if (s == PG_OK) s = check_row_bytes(row_bytes);
+  if (s != PG_OK) return s;
+  if (L->T == 0) return PG_OK;
+  if (!padded || !packed) return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e = pg_launch_unpad(*L, padded, max_len, row_bytes, packed, stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "unpad kernel launch");
 }
 
 pg_status pg_pack_rows(const pg_layout* L, const void* prefix, int32_t prefix_pad,

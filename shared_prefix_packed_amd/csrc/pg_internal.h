@@ -48,6 +48,7 @@ struct pg_layout {
   std::vector<int32_t> tok_owner;      // [T] group of a prompt token, response index of a response token
   std::vector<int32_t> suffix_group;   // [N] group of each response
   int32_t max_prefix_len = 0, max_suffix_len = 0;
+  int32_t max_group_len = 0;           // longest packed group row (padded-form width)
   std::vector<double> inv_freq;     // [d/2], theta^(-2i/d)
   int32_t max_position = -1;
   int64_t useful_pairs = 0, unpacked_pairs = 0;
@@ -111,6 +112,12 @@ hipError_t pg_launch_pack(const pg_layout& L, const void* prefix, int32_t prefix
 hipError_t pg_launch_unpack(const pg_layout& L, const void* packed, int64_t row_bytes,
                             void* prefix_out, int32_t prefix_pad, void* suffix_out,
                             int32_t suffix_pad, hipStream_t stream);
+hipError_t pg_launch_positions_padded(const pg_layout& L, int32_t max_len, int64_t* pos,
+                                      uint8_t* mask, hipStream_t stream);
+hipError_t pg_launch_pad(const pg_layout& L, const void* packed, int64_t row_bytes, void* padded,
+                         int32_t max_len, hipStream_t stream);
+hipError_t pg_launch_unpad(const pg_layout& L, const void* padded, int32_t max_len,
+                           int64_t row_bytes, void* packed, hipStream_t stream);
 hipError_t pg_launch_attn_decode(const pg_layout& L, const void* q, const void* k, const void* v,
                                  const int32_t* cur_lens, void* o, float* lse, void* workspace,
                                  pg_dtype dtype, float softmax_scale, hipStream_t stream);

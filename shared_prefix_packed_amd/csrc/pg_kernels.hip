@@ -426,6 +426,72 @@ hipError_t pg_launch_decode_rowwise(const pg_layout& L, const void* q, const voi
 }
 
 namespace {
+// ------------------------------------------------------ right-padded form --
+// [G, max_len] rows: row g is group g's packed row [group_off[g],
+// group_off[g + 1]), then padding (verl page, sections 1-2). No tables (a
+// layout without tokens): every group is empty.
+
+// One thread per (g, j): the packed position of token group_off[g] + j, or 0
+// on padding; mask 1 on real tokens.
+__global__ __launch_bounds__(256) void positions_padded_kernel(
+    const int32_t* __restrict__ group_off, const int32_t* __restrict__ g0a,
+    const int32_t* __restrict__ pea, const int32_t* __restrict__ ssa, int64_t* __restrict__ pos,
+    uint8_t* __restrict__ mask, int64_t G, int32_t max_len) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= G * max_len) return;
+  const int64_t g = e / max_len;
+  const int32_t j = int32_t(e - g * max_len);
+  int64_t p = 0;
+  bool real = false;
+  if (group_off) {
+    const int32_t a = group_off[g];
+    if (j < group_off[g + 1] - a) {
+      const int32_t t = a + j, pe = pea[t], g0 = g0a[t];
+      p = t < pe ? int64_t(t - g0) : int64_t(pe - g0) + int64_t(t - ssa[t]);
+      real = true;
+    }
+  }
+  pos[e] = p;
+  if (mask) mask[e] = real ? 1 : 0;
+}
+
+// One wave per padded row (g, j): the packed row, or zeros on padding.
+template <typename U>
+__global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict__ group_off,
+                                                       const U* packed, U* padded, int64_t G,
+                                                       int32_t max_len, int64_t upr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = G * max_len;
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x >> 6);
+  for (int64_t row = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); row < rows;
+       row += nw) {
+    const int64_t g = row / max_len;
+    const int32_t j = int32_t(row - g * max_len);
+    U* dst = padded + row * upr;
+    const int32_t a = group_off ? group_off[g] : 0;
+    if (group_off && j < group_off[g + 1] - a)
+      copy_row(packed + (int64_t(a) + j) * upr, dst, upr, lane);
+    else
+      zero_row(dst, upr, lane);
+  }
+}
+
+// One wave per packed row t: its group (prompt tokens carry it as owner,
+// response tokens through their response) and index t - g0 in the group row.
+template <typename U>
+__global__ __launch_bounds__(256) void unpad_rows_kernel(
+    const int32_t* __restrict__ owner, const int32_t* __restrict__ suffix_group,
+    const int32_t* __restrict__ g0a, const int32_t* __restrict__ pea, const U* padded, U* packed,
+    int64_t T, int32_t max_len, int64_t upr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x >> 6);
+  for (int64_t t = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); t < T; t += nw) {
+    const int32_t o = owner[t];
+    const int64_t g = t < pea[t] ? o : suffix_group[o];
+    copy_row(padded + (g * max_len + (t - g0a[t])) * upr, packed + t * upr, upr, lane);
+  }
+}
+
 // Four rows (waves) per 256-thread block, at most 8192 blocks (32 waves per CU).
 dim3 gather_grid(int64_t rows) {
   const int64_t blocks = (rows + 3) / 4;
@@ -470,5 +536,45 @@ hipError_t pg_launch_unpack(const pg_layout& L, const void* packed, int64_t row_
         go, L.d_prefix_lens, L.d_seg_off, L.d_suffix_group, L.d_suffix_lens,
         static_cast<const uint32_t*>(packed), static_cast<uint32_t*>(prefix_out), G, prefix_pad,
         static_cast<uint32_t*>(suffix_out), N, suffix_pad, row_bytes / 4);
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_positions_padded(const pg_layout& L, int32_t max_len, int64_t* pos,
+                                      uint8_t* mask, hipStream_t stream) {
+  const int64_t G = int64_t(L.group_off.size()) - 1, n = G * max_len;
+  if (n == 0) return hipSuccess;
+  const bool have = L.T > 0;
+  positions_padded_kernel<<<dim3(uint32_t((n + 255) / 256)), dim3(256), 0, stream>>>(
+      have ? L.d_group_off : nullptr, L.d_g0, L.d_pe, L.d_ss, pos, mask, G, max_len);
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_pad(const pg_layout& L, const void* packed, int64_t row_bytes, void* padded,
+                         int32_t max_len, hipStream_t stream) {
+  const int64_t G = int64_t(L.group_off.size()) - 1, rows = G * max_len;
+  if (rows == 0) return hipSuccess;
+  const int32_t* go = L.T > 0 ? L.d_group_off : nullptr;
+  if (row_bytes % 16 == 0)
+    pad_rows_kernel<uint4><<<gather_grid(rows), dim3(256), 0, stream>>>(
+        go, static_cast<const uint4*>(packed), static_cast<uint4*>(padded), G, max_len,
+        row_bytes / 16);
+  else
+    pad_rows_kernel<uint32_t><<<gather_grid(rows), dim3(256), 0, stream>>>(
+        go, static_cast<const uint32_t*>(packed), static_cast<uint32_t*>(padded), G, max_len,
+        row_bytes / 4);
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_unpad(const pg_layout& L, const void* padded, int32_t max_len,
+                           int64_t row_bytes, void* packed, hipStream_t stream) {
+  if (L.T == 0) return hipSuccess;
+  if (row_bytes % 16 == 0)
+    unpad_rows_kernel<uint4><<<gather_grid(L.T), dim3(256), 0, stream>>>(
+        L.d_owner, L.d_suffix_group, L.d_g0, L.d_pe, static_cast<const uint4*>(padded),
+        static_cast<uint4*>(packed), L.T, max_len, row_bytes / 16);
+  else
+    unpad_rows_kernel<uint32_t><<<gather_grid(L.T), dim3(256), 0, stream>>>(
+        L.d_owner, L.d_suffix_group, L.d_g0, L.d_pe, static_cast<const uint32_t*>(padded),
+        static_cast<uint32_t*>(packed), L.T, max_len, row_bytes / 4);
   return hipGetLastError();
 }

@@ -186,6 +186,9 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
     }
     L.group_off[num_groups] = cur;
     L.seg_off.push_back(cur);
+    L.max_group_len = 0;
+    for (int32_t g = 0; g < num_groups; ++g)
+      L.max_group_len = std::max(L.max_group_len, L.group_off[g + 1] - L.group_off[g]);
 
     // ------------------------------------------------ rotary frequencies --
     L.inv_freq.resize(size_t(head_dim / 2));

@@ -437,3 +437,27 @@ def test_single_pair_rope_argument_errors():
     lay = pg.pg_build_layout_host([5], [1], [3], 4, 1, 128, 1e4)
     # argument checks need a device copy; they are exercised on the GPU
     assert lib.pg_rope(lay.handle, dummy, None, None, None, None, 1, None) == -5
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_max_group_len_matches_oracle(shape):
+    P, S = shape
+    L = _build(P, S)
+    n, flat = _flat(S)
+    gl = O.group_lens(O.layout(P, n, flat))
+    assert L.summary().max_group_len == (int(gl.max()) if gl.size else 0)
+    assert L.summary().reserved == 0
+
+
+def test_padded_form_argument_errors():
+    lib = _lib.load()
+    dummy = ctypes.c_void_p(16)
+    L = _build([5], [[3]])
+    assert lib.pg_position_ids_padded(L.handle, 8, dummy, None, None) == -5   # not uploaded
+    assert lib.pg_pad_rows(L.handle, dummy, 16, dummy, 8, None) == -5
+    assert lib.pg_unpad_rows(L.handle, dummy, 8, 16, dummy, None) == -5
+    E = _build([0, 0], [[0], []])   # no tokens: argument checks still apply
+    assert lib.pg_pad_rows(E.handle, None, 6, dummy, 4, None) == -1          # row bytes
+    assert lib.pg_unpad_rows(E.handle, None, 4, 0, None, None) == -1         # row bytes
+    assert lib.pg_position_ids_padded(E.handle, -1, dummy, None, None) == -1  # width
+    assert lib.pg_position_ids_padded(None, 4, dummy, None, None) == -1
