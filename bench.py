@@ -305,6 +305,28 @@ def main(argv=None):
             tc.append((a_, b_))
         torch.cuda.synchronize()
         cms = float(np.mean([x.elapsed_time(y) for x, y in tc]))
+        # the right-padded form [G, max_len] of the same rows, and back
+        Lp = build()
+        width = Lp.summary().max_group_len
+        padded = torch.empty((Gn, width, hidden), dtype=torch.bfloat16, device="cuda")
+        back = torch.empty_like(packed)
+        for _ in range(2):
+            pg.pg_pad_rows(Lp, packed, padded=padded, stream=stream)
+            pg.pg_unpad_rows(Lp, padded, packed=back, stream=stream)
+        tpa, tun = [], []
+        for _ in range(20):
+            a_, b_, c_ = ev(), ev(), ev()
+            a_.record(stream)
+            pg.pg_pad_rows(Lp, packed, padded=padded, stream=stream)
+            b_.record(stream)
+            pg.pg_unpad_rows(Lp, padded, packed=back, stream=stream)
+            c_.record(stream)
+            tpa.append((a_, b_))
+            tun.append((b_, c_))
+        torch.cuda.synchronize()
+        pad_ms = float(np.mean([x.elapsed_time(y) for x, y in tpa]))
+        unpad_ms = float(np.mean([x.elapsed_time(y) for x, y in tun]))
+        Lp.close()
         pms = float(np.mean([x.elapsed_time(y) for x, y in tp]))
         ums = float(np.mean([x.elapsed_time(y) for x, y in tu]))
         rb = hidden * 2
@@ -314,9 +336,14 @@ def main(argv=None):
                    "pack_ms": round(pms, 4), "pack_gbs": round(pack_bytes / (pms * 1e-3) / 1e9, 1),
                    "unpack_ms": round(ums, 4), "unpack_gbs": round(unpack_bytes / (ums * 1e-3) / 1e9, 1),
                    "device_copy_gbs": round(pack_bytes / (cms * 1e-3) / 1e9, 1),
+                   "padded_width": int(width),
+                   "pad_ms": round(pad_ms, 4),
+                   "pad_gbs": round((T + Gn * width) * rb / (pad_ms * 1e-3) / 1e9, 1),
+                   "unpad_ms": round(unpad_ms, 4),
+                   "unpad_gbs": round(2 * T * rb / (unpad_ms * 1e-3) / 1e9, 1),
                    "hbm_peak_gbs": PEAK_HBM_GBS}
         L.close()
-        del pre, suf, packed, outs, cpy
+        del pre, suf, packed, outs, cpy, padded, back
 
     # one decode step with this batch's layout taken as the KV cache (response
     # segments at capacity, current lengths drawn in [1, capacity])
