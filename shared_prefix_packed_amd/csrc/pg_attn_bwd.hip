@@ -22,7 +22,10 @@
 //  * bwd_dkv_kernel: key blocks of at most 128 keys of one KV head inside one
 //    segment. The queries that read key j are one contiguous range [j, qend)
 //    (the group's end for a prompt key, the response's end otherwise), taken
-//    in tiles of 64 rows for each of the r query heads. Per wave 32 keys:
+//    in tiles of 64 rows for each of the r query heads, from the top down: the
+//    blocks of one segment share that end, so blocks running side by side on
+//    an XCD read the same Q and dO tiles at about the same time. Per wave 32
+//    keys:
 //      S = Q K^T, dP = dO V^T                (A = Q, dO rows from LDS)
 //      P, dS as above (lse and D per query row from LDS)
 //      dV += P^T dO, dK += dS^T Q           (A = P^T, dS^T from the
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) goff[i] = rowmajor_off(4 * wave + i, lane, q_row_bytes);
   auto fetch = [&](int n, int stage) {
-    const int m = n / a.r, h = hk * a.r + n % a.r;
+    const int m = nq - 1 - n / a.r, h = hk * a.r + n % a.r;   // query tiles from the top down
     const int q0 = q_start + KV_QT * m;
     const int rows = min(KV_QT, it.qend - q0);
     const int bytes = (rows - 1) * q_row_bytes + D * 2;
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     bare_barrier();
     if (n + 2 < ntiles) fetch(n + 2, (n + 2) % KV_NSTAGE);
     if (!wave_keys) continue;
-    const int q0 = q_start + KV_QT * (n / a.r);
+    const int q0 = q_start + KV_QT * (nq - 1 - n / a.r);
     // rows of this tile that can read any of the wave's keys
     if (q0 + KV_QT - 1 < kw0) continue;
     const unsigned char* st = smem + (n % KV_NSTAGE) * KV_STAGE;
