@@ -24,15 +24,15 @@
 //    (the group's end for a prompt key, the response's end otherwise), taken
 //    in tiles of 64 rows for each of the r query heads, from the top down: the
 //    blocks of one segment share that end, so blocks running side by side on
-//    an XCD read the same Q and dO tiles at about the same time. Per wave 32
-//    keys:
-//      S = Q K^T, dP = dO V^T                (A = Q, dO rows from LDS)
-//      P, dS as above (lse and D per query row from LDS)
-//      dV += P^T dO, dK += dS^T Q           (A = P^T, dS^T from the
-//                                            accumulators, B = dO, Q by
-//                                            transposing LDS reads)
-//    so K, V, dK and dV stay in registers for the whole block and no atomics
-//    are needed.
+//    an XCD read the same Q and dO tiles at about the same time. Each 32-key
+//    slice is taken by two waves that share a SIMD:
+//      dV wave: S = Q K^T, P, dV += P^T dO
+//      dK wave: S = Q K^T, dP = dO V^T, dS = P (dP - D), dK += dS^T Q
+//    (A = Q, dO rows from LDS, B = K, V in registers; A = P^T, dS^T from the
+//    accumulators, B = dO, Q by transposing LDS reads; lse and D per query
+//    row from LDS). Each wave holds half the operands, which lets two fit on a
+//    SIMD; K, V, dK and dV stay in registers for the whole block and no
+//    atomics are needed.
 // Tiles go HBM -> LDS with buffer loads that write LDS (as in the forward),
 // four (dQ) or three (dK, dV) stages deep, with one workgroup barrier per tile.
 #include <hip/hip_runtime.h>
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   // A operand reads: row-major K/V row 32 kb + qi, chunk 2 ks + half (swizzled)
   int koff[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * 256 + 16 * ((2 * ks + half) ^ (qi & 15));
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * 256 + 16 * ((2 * ks + half) ^ rm_swz(qi));
   const TrOffsets tro(lane);
 
   f32x16_t dqacc[4];
@@ -361,121 +361,106 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
 // ------------------------------------------------------------------ dK, dV --
 
 constexpr int KV_QT = 64;                    // query rows per tile
-constexpr int KV_WAVES = 4;                  // 32 keys each (PG_KV_BLOCK = 128)
+constexpr int KV_WAVES = 8;                  // 4 dV waves + 4 dK waves, 32 keys each
 constexpr int KV_REGION = KV_QT * D * 2;     // 16 KB
 constexpr int KV_ROWS = 2 * KV_REGION;       // Q, dO row-major
 constexpr int KV_STAGE = KV_ROWS + 3 * 256;  // + lse, D, and a sink for unused lanes' loads
 constexpr int KV_NSTAGE = 3;
-constexpr int KV_LOADS = 9;                  // per wave per tile: 8 x 1 KB + one 256 B load
+constexpr int KV_LOADS = 5;                  // per wave per tile: 4 x 1 KB + one 256 B load
 
-static_assert(KV_WAVES * 32 == PG_KV_BLOCK, "key block = waves x 32 keys");
+static_assert((KV_WAVES / 2) * 32 == PG_KV_BLOCK, "key block = 4 slices x 32 keys");
 
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[KV_NSTAGE * KV_STAGE];
+// Waves 0-3 and 4-7 take the same four 32-key slices: the first four compute
+// dV (S, P, dV += P^T dO), the last four dK (S, dP, dS, dK += dS^T Q). Each
+// role runs its own loop and holds only its own operands and accumulators, so
+// two waves fit on a SIMD (waves w and w + 4 share one) and hide each other's
+// latency; S is computed by both roles. Both loops take the same barriers.
+struct KvCtx {
+  const pg_kv_item* it;
+  int lane, wave, col, half, hk, kw0, kw1, key, q_start, nq, ntiles, q_row_bytes;
+  bool wave_keys;
+  uint32_t lds_base;
+  int goff[2];
+};
 
-  const pg_kv_item it = a.kv_items[blockIdx.x];
-  if (it.k1 <= it.k0) return;   // padding
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31;    // key of this lane inside the wave's 32
-  const int half = lane >> 5;
+__device__ inline void kv_fetch(const BwdArgs& a, const KvCtx& c, int n, int stage) {
+  const int m = c.nq - 1 - n / a.r, h = c.hk * a.r + n % a.r;   // query tiles from the top down
+  const int q0 = c.q_start + KV_QT * m;
+  const int rows = min(KV_QT, c.it->qend - q0);
+  const int bytes = (rows - 1) * c.q_row_bytes + D * 2;
+  const int64_t row0 = (int64_t(q0) * a.Hq + h) * D;
+  const i32x4_t rq = make_rsrc(a.q + row0, bytes);
+  const i32x4_t rd = make_rsrc(a.dout + row0, bytes);
+  const uint32_t sb = c.lds_base + uint32_t(stage * KV_STAGE) + 2048 * c.wave;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) buf16_to_lds(rq, c.goff[i], sb + 1024 * i);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) buf16_to_lds(rd, c.goff[i], sb + KV_REGION + 1024 * i);
+  // lse (wave 0) or D (wave 1) of the tile's rows; the other waves load
+  // nothing into the sink, so that every wave waits for the same count
+  const float* src = c.wave == 0 ? a.lse : a.delta;
+  const i32x4_t rl = make_rsrc(src + int64_t(h) * a.T + q0, c.wave < 2 ? 4 * rows : 0);
+  buf4_to_lds(rl, 4 * c.lane, c.lds_base + uint32_t(stage * KV_STAGE) + KV_ROWS + 256 * min(c.wave, 2));
+}
 
-  const int hk = it.hk;
-  const int kw0 = it.k0 + 32 * wave;
-  const int kw1 = min(kw0 + 32, it.k1);
-  const bool wave_keys = kw0 < kw1;
-  const int key = kw0 + col;
-  const bool key_valid = key < kw1;
-
-  // K and V rows of the wave's keys as B operands (lane: key col,
-  // d = 16 ks + 8 half + 0..7); keys past the block read as zeros
-  bf16x8_t kf[8], vf[8];
+template <bool KWAVE>
+__device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* smem) {
+  const pg_kv_item& it = *c.it;
+  // K (both roles) and V (dK role) rows of the slice's keys as B operands
+  // (lane: key col, d = 16 ks + 8 half + 0..7); keys past the block are zero
+  bf16x8_t kf[8], vf[KWAVE ? 8 : 1];
   {
-    const int64_t base = (int64_t(key_valid ? key : it.k0) * a.Hkv + hk) * D + 8 * half;
+    const bool key_valid = c.key < c.kw1;
+    const int64_t base = (int64_t(key_valid ? c.key : it.k0) * a.Hkv + c.hk) * D + 8 * c.half;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint4 zk = key_valid ? ldg16(a.k + base + 16 * ks) : make_uint4(0, 0, 0, 0);
-      const uint4 zv = key_valid ? ldg16(a.v + base + 16 * ks) : make_uint4(0, 0, 0, 0);
-      kf[ks] = as_bf16x8(zk);
-      vf[ks] = as_bf16x8(zv);
+      kf[ks] = as_bf16x8(key_valid ? ldg16(a.k + base + 16 * ks) : make_uint4(0, 0, 0, 0));
+      if constexpr (KWAVE)
+        vf[ks] = as_bf16x8(key_valid ? ldg16(a.v + base + 16 * ks) : make_uint4(0, 0, 0, 0));
     }
     // waited for once, here, not inside the tile loop (see bwd_dq_kernel)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(kf[ks]), "+v"(vf[ks]));
-  }
-
-  f32x16_t dkacc[4], dvacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dkacc[db][i] = 0.f;
-      dvacc[db][i] = 0.f;
+    for (int ks = 0; ks < 8; ++ks) {
+      asm volatile("" : "+v"(kf[ks]));
+      if constexpr (KWAVE) asm volatile("" : "+v"(vf[ks]));
     }
-
-  // query tiles: rows q0 = k0 + 64 m (m < nq) for each query head of hk
-  const int q_start = it.k0;
-  const int nq = (it.qend - q_start + KV_QT - 1) / KV_QT;
-  const int ntiles = nq * a.r;
-  const int q_row_bytes = a.Hq * D * 2;
-
-  // staging: wave w brings blocks 4 w .. 4 w + 3 of the row-major Q and dO
-  // tiles and one 256 B row: wave 0 the rows' lse, wave 1 their D, waves 2-3
-  // an empty load into the sink
-  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
-  int goff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) goff[i] = rowmajor_off(4 * wave + i, lane, q_row_bytes);
-  auto fetch = [&](int n, int stage) {
-    const int m = nq - 1 - n / a.r, h = hk * a.r + n % a.r;   // query tiles from the top down
-    const int q0 = q_start + KV_QT * m;
-    const int rows = min(KV_QT, it.qend - q0);
-    const int bytes = (rows - 1) * q_row_bytes + D * 2;
-    const int64_t row0 = (int64_t(q0) * a.Hq + h) * D;
-    const i32x4_t rq = make_rsrc(a.q + row0, bytes);
-    const i32x4_t rd = make_rsrc(a.dout + row0, bytes);
-    const uint32_t sb = lds_base + uint32_t(stage * KV_STAGE) + 4096 * wave;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) buf16_to_lds(rq, goff[i], sb + 1024 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) buf16_to_lds(rd, goff[i], sb + KV_REGION + 1024 * i);
-    // the tile's 64 lse (wave 0) or D (wave 1) values; lanes past the rows
-    // read zeros
-    const float* src = wave == 0 ? a.lse : a.delta;
-    const i32x4_t rl = make_rsrc(src + int64_t(h) * a.T + q0, wave < 2 ? 4 * rows : 0);
-    buf4_to_lds(rl, 4 * lane, lds_base + uint32_t(stage * KV_STAGE) + KV_ROWS + 256 * min(wave, 2));
-  };
-
+  }
   // A operand reads of row-major Q / dO: row 32 kb + col, chunk 2 ks + half
   int aoff[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) aoff[ks] = col * 256 + 16 * ((2 * ks + half) ^ (col & 15));
-  const TrOffsets tro(lane);
+  for (int ks = 0; ks < 8; ++ks) aoff[ks] = c.col * 256 + 16 * ((2 * ks + c.half) ^ rm_swz(c.col));
+  const TrOffsets tro(c.lane);
 
-  fetch(0, 0);
-  if (ntiles > 1) fetch(1, 1);
+  f32x16_t acc[4];   // dV or dK: rows = keys (registers), lanes = d
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  for (int n = 0; n < ntiles; ++n) {
-    if (n + 1 < ntiles)
+  kv_fetch(a, c, 0, 0);
+  if (c.ntiles > 1) kv_fetch(a, c, 1, 1);
+
+  for (int n = 0; n < c.ntiles; ++n) {
+    if (n + 1 < c.ntiles)
       wait_vmem<KV_LOADS>();
     else
       wait_vmem<0>();
     bare_barrier();
-    if (n + 2 < ntiles) fetch(n + 2, (n + 2) % KV_NSTAGE);
-    if (!wave_keys) continue;
-    const int q0 = q_start + KV_QT * (nq - 1 - n / a.r);
-    // rows of this tile that can read any of the wave's keys
-    if (q0 + KV_QT - 1 < kw0) continue;
+    if (n + 2 < c.ntiles) kv_fetch(a, c, n + 2, (n + 2) % KV_NSTAGE);
+    if (!c.wave_keys) continue;
+    const int q0 = c.q_start + KV_QT * (c.nq - 1 - n / a.r);
+    // rows of this tile that can read any of the slice's keys
+    if (q0 + KV_QT - 1 < c.kw0) continue;
     const unsigned char* st = smem + (n % KV_NSTAGE) * KV_STAGE;
+    const float* lse_t = reinterpret_cast<const float*>(st + KV_ROWS);
+    const float* dlt_t = reinterpret_cast<const float*>(st + KV_ROWS + 256);
+    const bool full = (q0 >= c.kw0 + 31) && (q0 + KV_QT <= it.qend);
 
-    f32x16_t sacc[2], pacc[2];
+    f32x16_t sacc[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sacc[0][i] = 0.f;
       sacc[1][i] = 0.f;
-      pacc[0][i] = 0.f;
-      pacc[1][i] = 0.f;
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -485,63 +470,118 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc[kb], 0, 0, 0);
       }
     sched_reads_ahead<4, 1, 16>();
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t ad =
-            as_bf16x8(*reinterpret_cast<const uint4*>(st + KV_REGION + 8192 * kb + aoff[ks]));
-        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], pacc[kb], 0, 0, 0);
-      }
-    sched_reads_ahead<4, 1, 16>();
 
-    // register i of block kb holds query row q0 + 32 kb + 8 (i/4) + 4 half + i%4
-    const float* lse_t = reinterpret_cast<const float*>(st + KV_ROWS);
-    const float* dlt_t = reinterpret_cast<const float*>(st + KV_ROWS + 256);
-    const bool full = (q0 >= kw0 + 31) && (q0 + KV_QT <= it.qend);
+    if constexpr (!KWAVE) {
+      // P; register i of block kb holds query row q0 + 32 kb + 8 (i/4) + 4 half + i%4
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = 32 * kb + 8 * g + 4 * half;
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
-        const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + r0);
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = 32 * kb + 8 * g + 4 * c.half;
+          const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * g + j;
-          const int qrow = q0 + r0 + j;
-          float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -(&l4.x)[j] * LOG2E));
-          if (!full) p = (qrow >= key && qrow < it.qend) ? p : 0.f;
-          pacc[kb][i] = p * (pacc[kb][i] - (&d4.x)[j]);   // dS
-          sacc[kb][i] = p;                                // P
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * g + j;
+            const int qrow = q0 + r0 + j;
+            float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -(&l4.x)[j] * LOG2E));
+            if (!full) p = (qrow >= c.key && qrow < it.qend) ? p : 0.f;
+            sacc[kb][i] = p;
+          }
         }
-      }
-    // dV += P^T dO, dK += dS^T Q (B by transposing reads of the row-major
-    // dO and Q tiles)
+      // dV += P^T dO (B by transposing reads of the row-major dO tile)
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const bf16x8_t pf = pack_step(sacc[s2 >> 1], s2);
-      const bf16x8_t dsf = pack_step(pacc[s2 >> 1], s2);
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const bf16x8_t pf = pack_step(sacc[s2 >> 1], s2);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, tr_rowmajor(st + KV_REGION, tro, s2, db),
-                                                            dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf, tr_rowmajor(st, tro, s2, db),
-                                                            dkacc[db], 0, 0, 0);
+        for (int db = 0; db < 4; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, tr_rowmajor(st + KV_REGION, tro, s2, db),
+                                                            acc[db], 0, 0, 0);
       }
+      sched_reads_ahead<4, 2, 16>();
+    } else {
+      f32x16_t pacc[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pacc[0][i] = 0.f;
+        pacc[1][i] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8_t ad =
+              as_bf16x8(*reinterpret_cast<const uint4*>(st + KV_REGION + 8192 * kb + aoff[ks]));
+          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], pacc[kb], 0, 0, 0);
+        }
+      sched_reads_ahead<4, 1, 16>();
+      // dS = P (dP - D)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = 32 * kb + 8 * g + 4 * c.half;
+          const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
+          const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + r0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * g + j;
+            const int qrow = q0 + r0 + j;
+            float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -(&l4.x)[j] * LOG2E));
+            if (!full) p = (qrow >= c.key && qrow < it.qend) ? p : 0.f;
+            pacc[kb][i] = p * (pacc[kb][i] - (&d4.x)[j]);
+          }
+        }
+      // dK += dS^T Q (B by transposing reads of the row-major Q tile)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const bf16x8_t dsf = pack_step(pacc[s2 >> 1], s2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf, tr_rowmajor(st, tro, s2, db),
+                                                            acc[db], 0, 0, 0);
+      }
+      sched_reads_ahead<4, 2, 16>();
     }
-    sched_reads_ahead<8, 2, 32>();
   }
 
   wait_vmem<0>();
   __syncthreads();
-  if (wave_keys) {
-    unsigned char* ot = smem + 16384 * wave;
+  if (c.wave_keys) {
+    unsigned char* ot = smem + 8192 * c.wave;
     const int64_t rs = int64_t(a.Hkv) * D;
-    store_tile<true>(dvacc, 1.f, ot, lane, a.dv + (int64_t(kw0) * a.Hkv + hk) * D, rs, kw1 - kw0);
-    store_tile<true>(dkacc, a.scale, ot + 8192, lane, a.dk + (int64_t(kw0) * a.Hkv + hk) * D, rs,
-                     kw1 - kw0);
+    uint16_t* dst = (KWAVE ? a.dk : a.dv) + (int64_t(c.kw0) * a.Hkv + c.hk) * D;
+    store_tile<true>(acc, KWAVE ? a.scale : 1.f, ot, c.lane, dst, rs, c.kw1 - c.kw0);
   }
+}
+
+__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[KV_NSTAGE * KV_STAGE];
+
+  const pg_kv_item it = a.kv_items[blockIdx.x];
+  if (it.k1 <= it.k0) return;   // padding
+  KvCtx c;
+  c.it = &it;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.col = c.lane & 31;
+  c.half = c.lane >> 5;
+  c.hk = it.hk;
+  c.kw0 = it.k0 + 32 * (c.wave & 3);
+  c.kw1 = min(c.kw0 + 32, it.k1);
+  c.wave_keys = c.kw0 < c.kw1;
+  c.key = c.kw0 + c.col;
+  c.q_start = it.k0;
+  c.nq = (it.qend - c.q_start + KV_QT - 1) / KV_QT;
+  c.ntiles = c.nq * a.r;
+  c.q_row_bytes = a.Hq * D * 2;
+  // staging: wave w brings blocks 2 w, 2 w + 1 of the row-major Q and dO tiles
+  c.lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) c.goff[i] = rowmajor_off(2 * c.wave + i, c.lane, c.q_row_bytes);
+  if (c.wave >= 4)
+    kv_loop<true>(a, c, smem);
+  else
+    kv_loop<false>(a, c, smem);
 }
 
 }  // namespace

@@ -115,10 +115,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecArgs a) {
     for (int b = 0; b < DEC_BLOCKS; ++b) buf16_to_lds(rv, goff[b], sb + DEC_REGION + 1024 * b);
   };
 
-  // A operand reads of K: row qi, stored chunk (2 ks + half) ^ (qi % 16)
+  // A operand reads of K: row qi, stored chunk (2 ks + half) ^ rm_swz(qi)
   int koff[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * 256 + 16 * ((2 * ks + half) ^ (qi & 15));
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * 256 + 16 * ((2 * ks + half) ^ rm_swz(qi));
   const TrOffsets tro(lane);
 
   f32x16_t oacc[4];

@@ -149,17 +149,29 @@ __device__ inline double rope_hi(double xl, double xh, double c, double s) {
 
 // ------------------------------------------- row-major tiles of 256-byte rows --
 
+// Chunk swizzle of a row-major tile (256-byte rows, sixteen 16-byte chunks):
+// global chunk c of row r sits at chunk c ^ swz(r), swz(r) the 4-bit rotation
+// of r % 16, ((r & 3) << 2) | ((r & 15) >> 2). A plain c ^ (r % 16) spreads
+// row-wise reads over all 64 banks too, but keeps the eight rows of a
+// transposing read (below) on two 4-chunk groups, 32 banks: twice the cycles.
+// The rotation gives those rows all four groups, and it is still a bijection
+// of r % 16, so row-wise reads of 16 consecutive rows stay conflict-free.
+__device__ inline int rm_swz(int row) {
+  const int r = row & 15;
+  return ((r & 3) << 2) | (r >> 2);
+}
+
 // Byte offset (from a tile's first row) of the 16-byte global unit that lane
 // `lane` of 1 KB block `b` brings into a row-major tile: row 4 b + lane / 16,
-// stored chunk lane % 16 holding global chunk (lane % 16) ^ (row % 16).
+// stored chunk lane % 16 holding global chunk (lane % 16) ^ rm_swz(row).
 __device__ inline int rowmajor_off(int b, int lane, int row_bytes) {
   const int row = 4 * b + (lane >> 4);
-  const int chunk = (lane & 15) ^ (row & 15);
+  const int chunk = (lane & 15) ^ rm_swz(row);
   return row * row_bytes + 16 * chunk;
 }
 
 // Lane offsets of the transposing reads that take MFMA operand fragments out
-// of a row-major tile (256-byte rows, 16-byte chunks XOR-swizzled by row % 16):
+// of a row-major tile (256-byte rows, 16-byte chunks swizzled by rm_swz(row)):
 // within each 16-lane group the lanes address a 4-row x 32-byte block, lane
 // 4 j + c pointing at 4 columns 4c..4c+3 of row j, so that lane n receives
 // column n of the 4 rows. For the 16-row step s (rows 16 s + 4 (lane / 32) +
@@ -175,8 +187,8 @@ struct TrOffsets {
     for (int db = 0; db < 4; ++db) {
       const int byte = 64 * db + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
       const int c16 = byte >> 4, within = byte & 15;
-      lo[db] = rlo * 256 + 16 * (c16 ^ (rlo & 15)) + within;
-      hi[db] = rhi * 256 + 16 * (c16 ^ (rhi & 15)) + within;
+      lo[db] = rlo * 256 + 16 * (c16 ^ rm_swz(rlo)) + within;
+      hi[db] = rhi * 256 + 16 * (c16 ^ rm_swz(rhi)) + within;
     }
   }
 };
