@@ -244,6 +244,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
     gload(ld.ka, ld.sp.k1, 1);
     ld.next(a.spans);
   }
+  // The scalar set-up of each fetch (tile bounds, buffer descriptor, LDS
+  // destination) is done one step early, in the VALU step, whose scalar unit
+  // is idle; the MFMA step then only issues the loads.
+  i32x4_t pend_rs = make_rsrc(gbase, 0);
+  uint32_t pend_dst = 0;
+  auto prep = [&](int tile) {
+    const int ka = __builtin_amdgcn_readfirstlane(ld.ka);
+    const int k1 = __builtin_amdgcn_readfirstlane(ld.sp.k1);
+    const int bytes = (k1 - ka - 1) * row_bytes + D * 2;
+    pend_rs = make_rsrc(gbase + int64_t(ka) * a.Hkv * D, bytes);
+    pend_dst = lds_base + uint32_t((tile % NSTAGE) * STAGE + region + 4096 * wg);
+    ld.next(a.spans);
+  };
+  if (ntiles > 2) prep(2);
   wait_vmem_all();
   __syncthreads();
 
@@ -282,6 +296,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       sched_reads_ahead<0, 2, 12>();
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+    // the first K operands of S(n), read while PV(n-1) runs
+    uint4 kpre[4];
+    {
+      const unsigned char* kbn = smem + (n % NSTAGE) * STAGE;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        kpre[j] = *reinterpret_cast<const uint4*>(kbn + 8192 * (j & 1) + koff[j >> 1]);
+    }
     // keep PV(n-1) ahead of S(n): P dies before the S accumulators are born
     __builtin_amdgcn_sched_barrier(0);
     s_part = false;
@@ -308,11 +330,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
 #pragma unroll
           for (int kb2 = 0; kb2 < 2; ++kb2) {
             const bf16x8_t av =
-                as_bf16x8(*reinterpret_cast<const uint4*>(kb + 8192 * kb2 + koff[ks]));
+                ks < 2 ? as_bf16x8(kpre[2 * ks + kb2])
+                       : as_bf16x8(*reinterpret_cast<const uint4*>(kb + 8192 * kb2 + koff[ks]));
             sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[kb2], 0, 0, 0);
           }
         }
-        sched_reads_ahead<4, 1, 16>();
+        sched_reads_ahead<0, 1, 12>();
       }
       cp.next(a.spans);
     }
@@ -320,8 +343,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
     // Tile n+2 replaces tile n-2 in the ring; its last reader (PV(n-2) of
     // group B) finished before the previous barrier.
     if (n + 2 < ntiles) {
-      gload(ld.ka, ld.sp.k1, (n + 2) % NSTAGE);
-      ld.next(a.spans);
+#pragma unroll
+      for (int i = 0; i < LOADS_PER_TILE; ++i) buf16_to_lds(pend_rs, goff[i], pend_dst + 1024 * i);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -408,6 +431,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       }
     }
     s_part = false;
+    if (n >= 0 && n + 3 < ntiles) prep(n + 3);   // the fetch of the next MFMA step
     // Tile n+1 (fetched by this group in M(n-1)) must have landed before the
     // barrier: it is read from the next step on. The fetch of tile n+2 (issued
     // in M(n), if that tile exists) may stay in flight.
