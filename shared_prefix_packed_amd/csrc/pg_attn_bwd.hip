@@ -25,16 +25,19 @@
 //    in tiles of 64 rows for each of the r query heads, from the top down: the
 //    blocks of one segment share that end, so blocks running side by side on
 //    an XCD read the same Q and dO tiles at about the same time. Each 32-key
-//    slice is taken by two waves that share a SIMD:
-//      dV wave: S = Q K^T, P, dV += P^T dO
-//      dK wave: S = Q K^T, dP = dO V^T, dS = P (dP - D), dK += dS^T Q
+//    slice is taken by two waves that share a SIMD, each tile in two halves
+//    split by a workgroup barrier:
+//      dV wave: S = Q K^T, P (to LDS, fp32)  |  dV += P^T dO
+//      dK wave: dP = dO V^T, dP - D          |  dS = P (dP - D), dK += dS^T Q
 //    (A = Q, dO rows from LDS, B = K, V in registers; A = P^T, dS^T from the
 //    accumulators, B = dO, Q by transposing LDS reads; lse and D per query
-//    row from LDS). Each wave holds half the operands, which lets two fit on a
-//    SIMD; K, V, dK and dV stay in registers for the whole block and no
-//    atomics are needed.
+//    row from LDS). P is computed once per slice and handed over through LDS,
+//    so each wave of the pair issues 32 MFMAs per tile; each holds half the
+//    operands, which lets two fit on a SIMD; K, V, dK and dV stay in
+//    registers for the whole block and no atomics are needed.
 // Tiles go HBM -> LDS with buffer loads that write LDS (as in the forward),
-// four (dQ) or three (dK, dV) stages deep, with one workgroup barrier per tile.
+// four (dQ) or three (dK, dV) stages deep, with one workgroup barrier per tile
+// (two in dK, dV).
 #include <hip/hip_runtime.h>
 
 #include "pg_hip_common.h"
@@ -371,10 +374,11 @@ constexpr int KV_LOADS = 5;                  // per wave per tile: 4 x 1 KB + on
 static_assert((KV_WAVES / 2) * 32 == PG_KV_BLOCK, "key block = 4 slices x 32 keys");
 
 // Waves 0-3 and 4-7 take the same four 32-key slices: the first four compute
-// dV (S, P, dV += P^T dO), the last four dK (S, dP, dS, dK += dS^T Q). Each
-// role runs its own loop and holds only its own operands and accumulators, so
-// two waves fit on a SIMD (waves w and w + 4 share one) and hide each other's
-// latency; S is computed by both roles. Both loops take the same barriers.
+// dV (S, P, dV += P^T dO), the last four dK (dP, dS = P (dP - D), dK += dS^T Q)
+// with the P of their slice's dV wave. Each role runs its own loop and holds
+// only its own operands and accumulators, so two waves fit on a SIMD (waves w
+// and w + 4 share one) and hide each other's latency. Both loops take the
+// same barriers: one when a tile's stage has landed, one when P is in LDS.
 struct KvCtx {
   const pg_kv_item* it;
   int lane, wave, col, half, hk, kw0, kw1, key, q_start, nq, ntiles, q_row_bytes;
@@ -403,33 +407,57 @@ __device__ inline void kv_fetch(const BwdArgs& a, const KvCtx& c, int n, int sta
   buf4_to_lds(rl, 4 * c.lane, c.lds_base + uint32_t(stage * KV_STAGE) + KV_ROWS + 256 * min(c.wave, 2));
 }
 
+// P of one (query tile, slice) in fp32, as the dV waves hand it to the dK
+// waves: float4 m (= 4 kb + g) of lane l at byte 1024 m + 16 l.
+constexpr int KV_PX = KV_NSTAGE * KV_STAGE;
+constexpr int KV_SMEM = KV_PX + 4 * 8192;
+
+// P = exp(S scale - lse) of the 64 x 32 tile in the accumulator layout, zero
+// where the row cannot read the key (only on tiles crossing the diagonal or
+// the item's last query row).
+template <bool MASK>
+__device__ inline void tile_p(f32x16_t (&s)[2], const float4 (&l4)[8], float c_log2, int q0,
+                              int half, int key, int qend) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        float p = fast_exp2(fmaf(s[kb][i], c_log2, -(&l4[4 * kb + g].x)[j] * LOG2E));
+        if constexpr (MASK) {
+          const int qrow = q0 + 32 * kb + 8 * g + 4 * half + j;
+          p = ((qrow >= key) & (qrow < qend)) ? p : 0.f;
+        }
+        s[kb][i] = p;
+      }
+}
+
 template <bool KWAVE>
 __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* smem) {
   const pg_kv_item& it = *c.it;
-  // K (both roles) and V (dK role) rows of the slice's keys as B operands
-  // (lane: key col, d = 16 ks + 8 half + 0..7); keys past the block are zero
-  bf16x8_t kf[8], vf[KWAVE ? 8 : 1];
+  // B operands of the first product, rows of the slice's keys (lane: key col,
+  // d = 16 ks + 8 half + 0..7; keys past the block are zero): K for S = Q K^T
+  // (dV role), V for dP = dO V^T (dK role)
+  bf16x8_t bf[8];
   {
     const bool key_valid = c.key < c.kw1;
+    const uint16_t* src = KWAVE ? a.v : a.k;
     const int64_t base = (int64_t(key_valid ? c.key : it.k0) * a.Hkv + c.hk) * D + 8 * c.half;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kf[ks] = as_bf16x8(key_valid ? ldg16(a.k + base + 16 * ks) : make_uint4(0, 0, 0, 0));
-      if constexpr (KWAVE)
-        vf[ks] = as_bf16x8(key_valid ? ldg16(a.v + base + 16 * ks) : make_uint4(0, 0, 0, 0));
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      bf[ks] = as_bf16x8(key_valid ? ldg16(src + base + 16 * ks) : make_uint4(0, 0, 0, 0));
     // waited for once, here, not inside the tile loop (see bwd_dq_kernel)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      asm volatile("" : "+v"(kf[ks]));
-      if constexpr (KWAVE) asm volatile("" : "+v"(vf[ks]));
-    }
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(bf[ks]));
   }
   // A operand reads of row-major Q / dO: row 32 kb + col, chunk 2 ks + half
   int aoff[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) aoff[ks] = c.col * 256 + 16 * ((2 * ks + c.half) ^ rm_swz(c.col));
   const TrOffsets tro(c.lane);
+  float4* const px = reinterpret_cast<float4*>(smem + KV_PX + 8192 * (c.wave & 3)) + c.lane;
 
   f32x16_t acc[4];   // dV or dK: rows = keys (registers), lanes = d
 #pragma unroll
@@ -447,101 +475,75 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
       wait_vmem<0>();
     bare_barrier();
     if (n + 2 < c.ntiles) kv_fetch(a, c, n + 2, (n + 2) % KV_NSTAGE);
-    if (!c.wave_keys) continue;
     const int q0 = c.q_start + KV_QT * (c.nq - 1 - n / a.r);
-    // rows of this tile that can read any of the slice's keys
-    if (q0 + KV_QT - 1 < c.kw0) continue;
+    // the slice has keys, and some row of the tile can read one of them
+    const bool active = c.wave_keys && q0 + KV_QT - 1 >= c.kw0;
     const unsigned char* st = smem + (n % KV_NSTAGE) * KV_STAGE;
-    const float* lse_t = reinterpret_cast<const float*>(st + KV_ROWS);
-    const float* dlt_t = reinterpret_cast<const float*>(st + KV_ROWS + 256);
-    const bool full = (q0 >= c.kw0 + 31) && (q0 + KV_QT <= it.qend);
 
+    // first half: S and P (dV role; P goes to LDS), dP - D (dK role)
     f32x16_t sacc[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sacc[0][i] = 0.f;
-      sacc[1][i] = 0.f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t aq = as_bf16x8(*reinterpret_cast<const uint4*>(st + 8192 * kb + aoff[ks]));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc[kb], 0, 0, 0);
-      }
-    sched_reads_ahead<4, 1, 16>();
-
-    if constexpr (!KWAVE) {
-      // P; register i of block kb holds query row q0 + 32 kb + 8 (i/4) + 4 half + i%4
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r0 = 32 * kb + 8 * g + 4 * c.half;
-          const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * g + j;
-            const int qrow = q0 + r0 + j;
-            float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -(&l4.x)[j] * LOG2E));
-            if (!full) p = (qrow >= c.key && qrow < it.qend) ? p : 0.f;
-            sacc[kb][i] = p;
-          }
-        }
-      // dV += P^T dO (B by transposing reads of the row-major dO tile)
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const bf16x8_t pf = pack_step(sacc[s2 >> 1], s2);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, tr_rowmajor(st + KV_REGION, tro, s2, db),
-                                                            acc[db], 0, 0, 0);
-      }
-      sched_reads_ahead<4, 2, 16>();
-    } else {
-      f32x16_t pacc[2];
+    if (active) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pacc[0][i] = 0.f;
-        pacc[1][i] = 0.f;
+        sacc[0][i] = 0.f;
+        sacc[1][i] = 0.f;
       }
+      const unsigned char* at = st + (KWAVE ? KV_REGION : 0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t ad =
-              as_bf16x8(*reinterpret_cast<const uint4*>(st + KV_REGION + 8192 * kb + aoff[ks]));
-          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], pacc[kb], 0, 0, 0);
+          const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(at + 8192 * kb + aoff[ks]));
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bf[ks], sacc[kb], 0, 0, 0);
         }
       sched_reads_ahead<4, 1, 16>();
-      // dS = P (dP - D)
+      // lse (dV role) or D (dK role) of rows 32 kb + 8 g + 4 half + 0..3
+      const float* rowv = reinterpret_cast<const float*>(st + KV_ROWS + (KWAVE ? 256 : 0));
+      float4 r4[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int m = 0; m < 8; ++m)
+        r4[m] = *reinterpret_cast<const float4*>(rowv + 32 * (m >> 2) + 8 * (m & 3) + 4 * c.half);
+      if constexpr (!KWAVE) {
+        const bool full = (q0 >= c.kw0 + 31) && (q0 + KV_QT <= it.qend);
+        if (full)
+          tile_p<false>(sacc, r4, a.c_log2, q0, c.half, c.key, it.qend);
+        else
+          tile_p<true>(sacc, r4, a.c_log2, q0, c.half, c.key, it.qend);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r0 = 32 * kb + 8 * g + 4 * c.half;
-          const float4 l4 = *reinterpret_cast<const float4*>(lse_t + r0);
-          const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + r0);
+        for (int m = 0; m < 8; ++m)
+          px[64 * m] = make_float4(sacc[m >> 2][4 * (m & 3)], sacc[m >> 2][4 * (m & 3) + 1],
+                                   sacc[m >> 2][4 * (m & 3) + 2], sacc[m >> 2][4 * (m & 3) + 3]);
+      } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * g + j;
-            const int qrow = q0 + r0 + j;
-            float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -(&l4.x)[j] * LOG2E));
-            if (!full) p = (qrow >= c.key && qrow < it.qend) ? p : 0.f;
-            pacc[kb][i] = p * (pacc[kb][i] - (&d4.x)[j]);
-          }
-        }
-      // dK += dS^T Q (B by transposing reads of the row-major Q tile)
+        for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const bf16x8_t dsf = pack_step(pacc[s2 >> 1], s2);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf, tr_rowmajor(st, tro, s2, db),
-                                                            acc[db], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) sacc[m >> 2][4 * (m & 3) + j] -= (&r4[m].x)[j];
       }
-      sched_reads_ahead<4, 2, 16>();
     }
+    // P is written before any dK wave reads it
+    if constexpr (!KWAVE) wait_lds();
+    bare_barrier();
+    if (!active) continue;
+
+    // second half: dV += P^T dO, or dS = P (dP - D) and dK += dS^T Q (B by
+    // transposing reads of the row-major dO / Q tile)
+    if constexpr (KWAVE) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float4 p4 = px[64 * m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[m >> 2][4 * (m & 3) + j] *= (&p4.x)[j];
+      }
+    }
+    const unsigned char* bt = st + (KWAVE ? 0 : KV_REGION);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const bf16x8_t pf = pack_step(sacc[s2 >> 1], s2);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, tr_rowmajor(bt, tro, s2, db), acc[db], 0, 0, 0);
+    }
+    sched_reads_ahead<4, 2, 16>();
   }
 
   wait_vmem<0>();
@@ -555,7 +557,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
 }
 
 __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[KV_NSTAGE * KV_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[KV_SMEM];
 
   const pg_kv_item it = a.kv_items[blockIdx.x];
   if (it.k1 <= it.k0) return;   // padding
