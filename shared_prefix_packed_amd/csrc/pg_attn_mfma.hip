@@ -25,9 +25,11 @@
 // exp per score) as the two products cost MFMA cycles, so the two must run at
 // the same time. Each wave alternates an MFMA step (PV of the previous tile,
 // then S of the current one) with a VALU step (softmax of the current tile).
-// Waves 0-3 (group A) and 4-7 (group B) are one step apart and every step ends
-// in a workgroup barrier. Waves w and w + 4 share a SIMD, so on each SIMD one
-// wave feeds the matrix cores while the other runs the softmax.
+// Waves 0-3 (group A) run [MFMA; VALU] per tile and waves 4-7 (group B)
+// [VALU; MFMA]; waves w and w + 4 share a SIMD, so on each SIMD one wave feeds
+// the matrix cores while the other runs the softmax. One workgroup barrier per
+// tile keeps the ring consistent (a second one between the steps cost more than
+// it brought).
 //
 // Staging. K and V tiles go from global memory straight into a four-stage LDS
 // ring (buffer loads that write LDS, no registers), issued two tiles ahead:
@@ -86,11 +88,10 @@ constexpr float RESCALE_SLACK = 8.0f;
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ inline void wait_vmem_but_one_tile() { __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE); }
 
-// End of a ping-pong step: the workgroup barrier alone. Tile fetches and LDS
-// reads may stay in flight across it (a __syncthreads() fence would drain
-// both): every LDS read is consumed by the step after the one that issued it
-// at the latest, and a ring stage is refilled two barriers after its last
-// read. The asm's memory clobber keeps the compiler from moving memory
+// End of a tile: the workgroup barrier alone. Tile fetches and LDS reads may
+// stay in flight across it (a __syncthreads() fence would drain both): every
+// LDS read is consumed by the step after the one that issued it at the
+// latest, and a ring stage is refilled one barrier after its last read. The asm's memory clobber keeps the compiler from moving memory
 // operations across; the scheduling barriers keep arithmetic on its side.
 __device__ inline void step_barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       cp.next(a.spans);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Tile n+2 replaces tile n-2 in the ring; its last reader (PV(n-2) of
-    // group B) finished before the previous barrier.
+    // Tile n+2 replaces tile n-2 in the ring; its last readers (PV(n-2) in
+    // M(n-1) of both groups) finished before the previous barrier.
     if (n + 2 < ntiles) {
 #pragma unroll
       for (int i = 0; i < LOADS_PER_TILE; ++i) buf16_to_lds(pend_rs, goff[i], pend_dst + 1024 * i);
@@ -432,28 +433,29 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
     }
     s_part = false;
     if (n >= 0 && n + 3 < ntiles) prep(n + 3);   // the fetch of the next MFMA step
-    // Tile n+1 (fetched by this group in M(n-1)) must have landed before the
-    // barrier: it is read from the next step on. The fetch of tile n+2 (issued
-    // in M(n), if that tile exists) may stay in flight.
+  };
+  // End of iteration n (both groups have issued M(n)): this wave's part of
+  // tile n+1 must have landed before the barrier, since both groups read tile
+  // n+1 after it; the fetch of tile n+2 (issued in M(n)) may stay in flight.
+  auto end_of_iteration = [&](const int n) {
     if (n + 2 < ntiles)
       wait_vmem_but_one_tile();
     else
       wait_vmem_all();
+    step_barrier();
   };
 
   if (grp == 0) {
     for (int n = 0; n <= ntiles; ++n) {
       mfma_step(n);
-      step_barrier();
       valu_step(n);
-      step_barrier();
+      end_of_iteration(n);
     }
   } else {
     for (int n = 0; n <= ntiles; ++n) {
       valu_step(n - 1);
-      step_barrier();
       mfma_step(n);
-      step_barrier();
+      end_of_iteration(n);
     }
   }
 
