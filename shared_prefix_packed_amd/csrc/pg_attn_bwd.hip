@@ -18,7 +18,9 @@
 //      dQ^T += K^T dS^T                     (A = K^T by transposing LDS reads,
 //                                            B = dS^T from the accumulators)
 //    so Q, dO and dQ stay in registers and each key tile is staged once for
-//    the eight waves.
+//    the eight waves. Waves 4-7 run half a tile behind waves 0-3 (P, dS and
+//    the dQ product of the previous tile, then S and dP of this one), so the
+//    two waves of a SIMD do not reach the softmax at the same time.
 //  * bwd_dkv_kernel: key blocks of at most 128 keys of one KV head inside one
 //    segment. The queries that read key j are one contiguous range [j, qend)
 //    (the group's end for a prompt key, the response's end otherwise), taken
@@ -36,8 +38,8 @@
 //    operands, which lets two fit on a SIMD; K, V, dK and dV stay in
 //    registers for the whole block and no atomics are needed.
 // Tiles go HBM -> LDS with buffer loads that write LDS (as in the forward),
-// four (dQ) or three (dK, dV) stages deep, with one workgroup barrier per tile
-// (two in dK, dV).
+// four (dQ, fetched two tiles ahead) or three (dK, dV) stages deep, with one
+// workgroup barrier per tile (two in dK, dV).
 #include <hip/hip_runtime.h>
 
 #include "pg_hip_common.h"
@@ -270,37 +272,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
 
   SpanTiles ld, cp;
   ld.init(a.spans, it.span0, it.nspan);
-  for (int n = 0; n < 3 && n < ntiles; ++n) {
+  for (int n = 0; n < 2 && n < ntiles; ++n) {
     fetch(ld.ka, ld.k1, n);
     ld.next(a.spans);
   }
   cp.init(a.spans, it.span0, it.nspan);
 
-  for (int n = 0; n < ntiles; ++n) {
-    // tile n landed (tiles n + 1, n + 2 may still be in flight); after the
-    // barrier every wave is done with tile n - 1, whose stage tile n + 3 takes
-    const int ahead = min(ntiles - 1 - n, 2);
-    if (ahead == 2)
-      wait_vmem<2 * Q_LOADS>();
-    else if (ahead == 1)
-      wait_vmem<Q_LOADS>();
-    else
-      wait_vmem<0>();
-    bare_barrier();
-    if (n + 3 < ntiles) {
-      fetch(ld.ka, ld.k1, (n + 3) % Q_NSTAGE);
-      ld.next(a.spans);
-    }
-    const int ka = cp.ka, k1 = cp.k1;
-    const bool is_prefix = k1 <= it.pe;
-    bool part = wave_active && ka <= te - 1;
-    if (!is_prefix) part = part && (__ballot(row_valid && ss_t == cp.k0) != 0ull);
-    const bool full = (ka + Q_KT <= k1) && (ka + Q_KT - 1 <= tb) && (is_prefix || ss_max <= ka);
-    cp.next(a.spans);
-    if (!part) continue;
-    const unsigned char* st = smem + (n % Q_NSTAGE) * Q_STAGE;
+  // Waves 0-3 take each tile whole in its iteration; waves 4-7 run half a tile
+  // behind: first P, dS and the dQ product of the previous tile, then S and dP
+  // of this one. The two waves of a SIMD (w and w + 4) thus feed the matrix
+  // cores and run the softmax at different times instead of together.
+  const bool lag = wave >= 4;
+  f32x16_t sacc[2], pacc[2];
+  bool h_part = false, h_full = true;   // second half pending: tile state
+  int h_lo = 0, h_hi = 0, h_stage = 0;
 
-    f32x16_t sacc[2], pacc[2];
+  auto first_half = [&](const unsigned char* st) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sacc[0][i] = 0.f;
@@ -325,11 +312,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
         pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], pacc[kb], 0, 0, 0);
       }
     sched_reads_ahead<4, 1, 16>();
-
-    // P^T and dS^T; register i of block kb holds key ka + 32 kb + 8 (i/4) + 4 half + i%4
-    const int base = ka + 4 * half;
-    const int lo = (is_prefix ? ka : ss_t) - base;
-    const int hi = min(tq, k1 - 1) - base;
+  };
+  // P^T and dS^T; register i of block kb holds key ka + 32 kb + 8 (i/4) + 4 half + i%4
+  auto second_half = [&](const unsigned char* st, bool full, int lo, int hi) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -342,7 +327,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
     bf16x8_t dsf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) dsf[ks] = pack_step(sacc[ks >> 1], ks);
-
     // dQ^T += K^T dS^T (K^T by transposing reads of the row-major K tile)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -351,6 +335,62 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
         dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rowmajor(st, tro, ks, db), dsf[ks],
                                                             dqacc[db], 0, 0, 0);
     sched_reads_ahead<6, 2, 16>();
+  };
+
+  // Start of iteration n: tile n landed (tile n + 1 may still be in flight);
+  // after the barrier every wave is done with tile n - 2 (the lagging waves
+  // finished it in the previous iteration), whose stage tile n + 2 takes.
+  // Returns the state of tile n (or none past the last tile).
+  auto begin_tile = [&](int n, bool& part, bool& full, int& lo, int& hi) {
+    if (n + 1 < ntiles)
+      wait_vmem<Q_LOADS>();
+    else
+      wait_vmem<0>();
+    bare_barrier();
+    if (n + 2 < ntiles) {
+      fetch(ld.ka, ld.k1, (n + 2) % Q_NSTAGE);
+      ld.next(a.spans);
+    }
+    part = false;
+    full = true;
+    lo = hi = 0;
+    if (n < ntiles) {
+      const int ka = cp.ka, k1 = cp.k1;
+      const bool is_prefix = k1 <= it.pe;
+      part = wave_active && ka <= te - 1;
+      if (!is_prefix) part = part && (__ballot(row_valid && ss_t == cp.k0) != 0ull);
+      full = (ka + Q_KT <= k1) && (ka + Q_KT - 1 <= tb) && (is_prefix || ss_max <= ka);
+      const int base = ka + 4 * half;
+      lo = (is_prefix ? ka : ss_t) - base;
+      hi = min(tq, k1 - 1) - base;
+      cp.next(a.spans);
+    }
+  };
+
+  if (!lag) {
+    for (int n = 0; n <= ntiles; ++n) {
+      bool part, full;
+      int lo, hi;
+      begin_tile(n, part, full, lo, hi);
+      if (part) {
+        const unsigned char* st = smem + (n % Q_NSTAGE) * Q_STAGE;
+        first_half(st);
+        second_half(st, full, lo, hi);
+      }
+    }
+  } else {
+    for (int n = 0; n <= ntiles; ++n) {
+      bool part, full;
+      int lo, hi;
+      begin_tile(n, part, full, lo, hi);
+      if (h_part) second_half(smem + h_stage * Q_STAGE, h_full, h_lo, h_hi);
+      if (part) first_half(smem + (n % Q_NSTAGE) * Q_STAGE);
+      h_part = part;
+      h_full = full;
+      h_lo = lo;
+      h_hi = hi;
+      h_stage = n % Q_NSTAGE;
+    }
   }
 
   // every wave is done with the ring before it holds the output tiles
