@@ -277,7 +277,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   // edge only P (group A) or only the S accumulators (group B) stay live.
   auto mfma_step = [&](const int n) {
     // MFMA step n: PV(n-1), S(n), then fetch tile n+2
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(3);   // the arbiter favours the wave feeding the matrix cores
     if (p_part) {
       const unsigned char* vb = smem + ((n - 1) % NSTAGE) * STAGE + voff;
 #pragma unroll
