@@ -523,6 +523,9 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
     // first half: S and P (dV role; P goes to LDS), dP - D (dK role)
     f32x16_t sacc[2];
     if (active) {
+      // MFMA blocks run at raised wave priority: the arbiter then favours
+      // whichever wave of the SIMD is feeding the matrix cores
+      __builtin_amdgcn_s_setprio(3);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sacc[0][i] = 0.f;
@@ -537,6 +540,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bf[ks], sacc[kb], 0, 0, 0);
         }
       sched_reads_ahead<4, 1, 16>();
+      __builtin_amdgcn_s_setprio(0);
       // lse (dV role) or D (dK role) of rows 32 kb + 8 g + 4 half + 0..3
       const float* rowv = reinterpret_cast<const float*>(st + KV_ROWS + (KWAVE ? 256 : 0));
       float4 r4[8];
@@ -576,6 +580,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
       }
     }
     const unsigned char* bt = st + (KWAVE ? 0 : KV_REGION);
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       const bf16x8_t pf = pack_step(sacc[s2 >> 1], s2);
@@ -584,6 +589,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, tr_rowmajor(bt, tro, s2, db), acc[db], 0, 0, 0);
     }
     sched_reads_ahead<4, 2, 16>();
+    __builtin_amdgcn_s_setprio(0);
   }
 
   wait_vmem<0>();
