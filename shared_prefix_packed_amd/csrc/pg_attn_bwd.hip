@@ -539,7 +539,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
           const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(at + 8192 * kb + aoff[ks]));
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bf[ks], sacc[kb], 0, 0, 0);
         }
-      sched_reads_ahead<4, 1, 16>();
+      sched_reads_ahead<6, 1, 16>();
       __builtin_amdgcn_s_setprio(0);
       // lse (dV role) or D (dK role) of rows 32 kb + 8 g + 4 half + 0..3
       const float* rowv = reinterpret_cast<const float*>(st + KV_ROWS + (KWAVE ? 256 : 0));
@@ -588,7 +588,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
       for (int db = 0; db < 4; ++db)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, tr_rowmajor(bt, tro, s2, db), acc[db], 0, 0, 0);
     }
-    sched_reads_ahead<4, 2, 16>();
+    sched_reads_ahead<6, 2, 16>();
     __builtin_amdgcn_s_setprio(0);
   }
 
