@@ -360,19 +360,23 @@ def main(argv=None):
         ws = torch.empty(max(1, L.decode_workspace_size()), dtype=torch.uint8, device="cuda")
 
         def time_decode(layout, kc, vc, work):
+            # steps back to back, as a decode loop issues them (the host's
+            # enqueue of step i+1 overlaps step i on the GPU), between one
+            # pair of events; the mean per step of three such runs
             for _ in range(3):
                 pg.pg_attn_decode(layout, qd, kc, vc, cur, w.softmax_scale, o=od, lse=ld,
                                   workspace=work, stream=stream)
             ts = []
-            for _ in range(20):
+            for _ in range(3):
                 a_, b_ = ev(), ev()
                 a_.record(stream)
-                pg.pg_attn_decode(layout, qd, kc, vc, cur, w.softmax_scale, o=od, lse=ld,
-                                  workspace=work, stream=stream)
+                for _ in range(20):
+                    pg.pg_attn_decode(layout, qd, kc, vc, cur, w.softmax_scale, o=od, lse=ld,
+                                      workspace=work, stream=stream)
                 b_.record(stream)
                 ts.append((a_, b_))
             torch.cuda.synchronize()
-            return float(np.mean([a_.elapsed_time(b_) for a_, b_ in ts]))
+            return float(np.mean([a_.elapsed_time(b_) / 20 for a_, b_ in ts]))
 
         dec_ms = time_decode(L, kr, v, ws)
         # algorithmic bytes: each group's prompt K/V once (groups with
