@@ -460,6 +460,8 @@ def main(argv=None):
             "rope": round(float(np.mean(rope_ms)), 4),
             "attn_fwd": round(attn_avg, 4),
         },
+        "attn_fwd_ms_stats": {"mean": round(attn_avg, 4), "median": round(float(np.median(attn_ms)), 4),
+                              "min": round(float(np.min(attn_ms)), 4), "reps": len(attn_ms)},
         "rope_gbs": round(2 * T * (Hq + Hkv) * d * q.element_size() / (np.mean(rope_ms) * 1e-3) / 1e9, 1),
         "unpacked_attn_ms": None if unpacked_ms is None else round(unpacked_ms, 4),
         "speedup_vs_unpacked": None if speedup is None else round(speedup, 3),
