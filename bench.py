@@ -127,7 +127,7 @@ def main(argv=None):
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(groups shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(groups would shard across GPUs with no exchange between them)", file=sys.stderr)
         return 2
 
     import numpy as np
