@@ -21,7 +21,7 @@ it belongs to. ``attention`` is that definition written out. ``attention_masked`
 is the packed form with an explicit key set per token, ``attention_dense`` the
 same with a dense T x T mask; tests tie all three together.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * RoPE is never defined on the pages: rotate-half convention on Q and K,
     omega_i = theta^(-2i/d), i < d/2.
   * softmax scale is an input (1/sqrt(d) in the workloads).
