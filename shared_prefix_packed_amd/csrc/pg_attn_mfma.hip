@@ -40,7 +40,7 @@
 // every 16-lane group owns 8 bytes; one such read then hands each lane 4 keys
 // of one d, which is exactly an MFMA A-operand fragment of V^T. The key order
 // inside each 16-key step is the one the S^T accumulators give P. A wave
-// issues the operand reads of its first four PV products at the end of its
+// issues the operand reads of its first two PV products at the end of its
 // VALU step, so the MFMA step starts without waiting on LDS.
 //
 // Output. The normalised O^T tile of each wave goes through LDS once the ring
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int j = 4 * ks + db;
-          const i16x4_t lo = j < 4 ? vpre[2 * j] : lds_read_tr(vb + 512 * (8 * ks + db));
-          const i16x4_t hi = j < 4 ? vpre[2 * j + 1] : lds_read_tr(vb + 512 * (8 * ks + 4 + db));
+          const i16x4_t lo = j < 2 ? vpre[2 * j] : lds_read_tr(vb + 512 * (8 * ks + db));
+          const i16x4_t hi = j < 2 ? vpre[2 * j + 1] : lds_read_tr(vb + 512 * (8 * ks + 4 + db));
           const bf16x8_t av = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks], acc[db], 0, 0, 0);
@@ -294,15 +294,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       }
       // issue order: 6 reads ahead, then (1 MFMA, 2 reads), so LDS latency
       // hides behind the matrix core instead of stalling it
-      sched_reads_ahead<0, 2, 12>();
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      sched_reads_ahead<0, 2, 14>();
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    // the first K operands of S(n), read while PV(n-1) runs
-    uint4 kpre[4];
+    // the K operands of the first S(n) step, read while PV(n-1) runs
+    uint4 kpre[2];
     {
       const unsigned char* kbn = smem + (n % NSTAGE) * STAGE;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         kpre[j] = *reinterpret_cast<const uint4*>(kbn + 8192 * (j & 1) + koff[j >> 1]);
     }
     // keep PV(n-1) ahead of S(n): P dies before the S accumulators are born
@@ -331,12 +331,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
 #pragma unroll
           for (int kb2 = 0; kb2 < 2; ++kb2) {
             const bf16x8_t av =
-                ks < 2 ? as_bf16x8(kpre[2 * ks + kb2])
+                ks < 1 ? as_bf16x8(kpre[2 * ks + kb2])
                        : as_bf16x8(*reinterpret_cast<const uint4*>(kb + 8192 * kb2 + koff[ks]));
             sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[kb2], 0, 0, 0);
           }
         }
-        sched_reads_ahead<0, 1, 12>();
+        sched_reads_ahead<0, 1, 14>();
       }
       cp.next(a.spans);
     }
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
       // was published before an earlier barrier
       const unsigned char* vb = smem + (n % NSTAGE) * STAGE + voff;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         vpre[2 * j] = lds_read_tr(vb + 512 * j);
         vpre[2 * j + 1] = lds_read_tr(vb + 512 * (4 + j));
       }
