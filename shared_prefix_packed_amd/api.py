@@ -344,18 +344,26 @@ def pg_pack_rows(layout: Layout, prefix, suffix, packed=None, stream=None):
     return packed
 
 
-def pg_unpack_rows(layout: Layout, packed, prefix_pad: int, suffix_pad: int, stream=None):
+def pg_unpack_rows(layout: Layout, packed, prefix_pad: int, suffix_pad: int, prefix_out=None,
+                   suffix_out=None, stream=None):
     """(prefix_out [G, prefix_pad, ...], suffix_out [N, suffix_pad + 1, ...]):
     the packed rows split back, each response part led by its group's last
-    prompt row."""
+    prompt row. Outputs given by the caller are filled in place (nothing is
+    allocated then, as under graph capture)."""
     import torch
     if not packed.is_contiguous():
         raise ValueError("packed must be contiguous")
     s = layout.summary()
     n_resp = int(np.asarray(layout.offsets()[1]).size - 1 - s.num_groups)
     tail = tuple(packed.shape[1:])
-    pre = torch.empty((s.num_groups, prefix_pad) + tail, dtype=packed.dtype, device=packed.device)
-    suf = torch.empty((n_resp, suffix_pad + 1) + tail, dtype=packed.dtype, device=packed.device)
+    pre_shape = (s.num_groups, prefix_pad) + tail
+    suf_shape = (n_resp, suffix_pad + 1) + tail
+    pre = prefix_out if prefix_out is not None else torch.empty(pre_shape, dtype=packed.dtype,
+                                                                device=packed.device)
+    suf = suffix_out if suffix_out is not None else torch.empty(suf_shape, dtype=packed.dtype,
+                                                                device=packed.device)
+    _check_tensor("prefix_out", pre, pre_shape, packed.dtype)
+    _check_tensor("suffix_out", suf, suf_shape, packed.dtype)
     check(load().pg_unpack_rows(layout.handle, ctypes.c_void_p(packed.data_ptr()),
                                 _row_bytes(packed, 1), ctypes.c_void_p(pre.data_ptr()),
                                 int(prefix_pad), ctypes.c_void_p(suf.data_ptr()), int(suffix_pad),
