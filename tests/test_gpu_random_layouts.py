@@ -2,7 +2,8 @@
 response lengths (zeros included), head shapes and tile-boundary lengths,
 each checked end to end against the fp64 oracle -- forward (O, lse), backward
 (dQ, dK, dV), one decode step, and the pack / unpack / pad / unpad gathers
-(bit-exact). Sizes stay small enough for the dense oracle."""
+(bit-exact) for bf16 with d = 128; forward and decode for fp32 (d = 64, 128)
+and bf16 d = 64. Sizes stay small enough for the dense oracle."""
 import numpy as np
 import pytest
 import torch
@@ -101,3 +102,53 @@ def test_random_layout_end_to_end(seed):
     assert np.array_equal(repacked.cpu().numpy(), rows.view(np.int32))
     assert np.array_equal(padded.cpu().numpy(), O.pad_rows(rows.view(np.int32), lay, width))
     assert np.array_equal(back.cpu().numpy(), rows.view(np.int32))
+
+
+def _to_dev(a, dtype):
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return dev(a)
+
+
+def _host(t, dtype):
+    return t.detach().cpu().numpy().astype(np.float64) if dtype == "f32" else host(t)
+
+
+def _f64(a, dtype):
+    return (a if dtype == "f32" else bf16_bits_to_f32(a)).astype(np.float64)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_layout_other_dtypes(seed):
+    """The same random layouts through the fp32 (d = 64, 128) and bf16 d = 64
+    kernels: forward and one decode step against the oracle (fp32: 1e-5)."""
+    P, S, hq, hkv = random_case(seed)
+    dtype, d = [("f32", 64), ("f32", 128), ("bf16", 64)][seed % 3]
+    w = make_custom(P, S, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                    seed=seed, name=f"random-{dtype}-{d}-{seed}")
+    print(f"random layout {seed} ({dtype}, d={d}): P={P} S={S} heads {hq}/{hkv}", flush=True)
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    L = pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, hq, hkv, d, w.rope_theta)
+    x = {n: draw_tensor(w, n) for n in ("q", "k", "v")}
+    q, k, v = (_to_dev(x[n], dtype) for n in ("q", "k", "v"))
+    tol_o, tol_l = (1e-5, 1e-5) if dtype == "f32" else (2e-2, 1e-3)
+    if w.total_tokens:
+        o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+        ro, rl = O.attention(_f64(x["q"], dtype), _f64(x["k"], dtype), _f64(x["v"], dtype), lay,
+                             w.softmax_scale, hq, hkv)
+        torch.cuda.synchronize()
+        assert np.abs(_host(o, dtype) - ro).max() <= tol_o
+        assert np.abs(lse.cpu().numpy() - rl).max() <= tol_l
+    if len(w.suffix_lens):
+        dx = draw_decode(w)
+        od, ld = pg.pg_attn_decode(L, _to_dev(dx["q"], dtype), k, v,
+                                   torch.from_numpy(dx["cur_lens"]).cuda(), w.softmax_scale)
+        rod, rld = O.decode_attention(_f64(dx["q"], dtype), _f64(x["k"], dtype), _f64(x["v"], dtype),
+                                      lay, dx["cur_lens"], w.softmax_scale, hq, hkv)
+        torch.cuda.synchronize()
+        empty = np.isneginf(rld)
+        assert np.array_equal(np.isneginf(ld.cpu().numpy()), empty)
+        assert np.abs(_host(od, dtype) - rod).max() <= tol_o
+        if (~empty).any():
+            assert np.abs(ld.cpu().numpy()[~empty] - rld[~empty]).max() <= tol_l
+    L.close()
