@@ -340,7 +340,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   // Start of iteration n: tile n landed (tile n + 1 may still be in flight);
   // after the barrier every wave is done with tile n - 2 (the lagging waves
   // finished it in the previous iteration), whose stage tile n + 2 takes.
-  // Returns the state of tile n (or none past the last tile).
+  // The state of tile n comes back through the references (none past the
+  // last tile).
   auto begin_tile = [&](int n, bool& part, bool& full, int& lo, int& hi) {
     if (n + 1 < ntiles)
       wait_vmem<Q_LOADS>();
