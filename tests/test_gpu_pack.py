@@ -58,3 +58,36 @@ def test_pack_unpack_edge_shapes(case):
     w = make_custom(P, S)
     for rt, (tail, dtype) in enumerate(ROW_TYPES):
         _check(w, tail, dtype, seed=100 + case)
+
+
+def test_gathers_larger_than_the_last_level_cache():
+    """Hidden-state rows (4 KB) on the GRPO-shaped workload: every gather
+    writes more than 256 MB, so the kernels take their streaming-store branch
+    (the cases above, all smaller, take the ordinary one)."""
+    w = make_workload(2)
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    G, N, T = len(w.prefix_lens), len(w.suffix_lens), int(w.total_tokens)
+    ppad, spad, row = int(w.prefix_lens.max()), int(w.suffix_lens.max()), 4096
+    assert T * row > 256 << 20
+    print(f"large gathers: {w.name} T={T}, {row}-byte rows", flush=True)
+    r = np.random.default_rng(77)
+    prefix = r.integers(0, 256, size=(G, ppad, row), dtype=np.uint8)
+    suffix = r.integers(0, 256, size=(N, spad, row), dtype=np.uint8)
+    L = pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
+                           w.num_kv_heads, w.head_dim, w.rope_theta)
+    packed = pg.pg_pack_rows(L, torch.from_numpy(prefix).cuda(), torch.from_numpy(suffix).cuda())
+    pre, suf = pg.pg_unpack_rows(L, packed, ppad, spad)
+    width = L.summary().max_group_len
+    padded = torch.full((G, width, row), 7, dtype=torch.uint8, device="cuda")
+    pg.pg_pad_rows(L, packed, padded=padded)
+    back = torch.full_like(packed, 9)
+    pg.pg_unpad_rows(L, padded, packed=back)
+    torch.cuda.synchronize()
+    want = O.pack_rows(prefix, suffix, lay)
+    assert np.array_equal(packed.cpu().numpy(), want)
+    wp, ws = O.unpack_rows(want, lay, ppad, spad)
+    assert np.array_equal(pre.cpu().numpy(), wp)
+    assert np.array_equal(suf.cpu().numpy(), ws)
+    assert np.array_equal(padded.cpu().numpy(), O.pad_rows(want, lay, width))
+    assert np.array_equal(back.cpu().numpy(), want)
+    L.close()
