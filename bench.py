@@ -276,7 +276,7 @@ def main(argv=None):
                "useful_tflops": round(bwd_tflops, 2),
                "pct_of_bf16_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
                "flop_definition": "10 * d * Hq per allowed (query, key) pair: S, dP, dV, dQ, dK products",
-               "kernels": "bwd_delta_kernel + bwd_dq_kernel + bwd_dkv_kernel, one pg_attn_bwd call"}
+               "kernels": "bwd_dq_kernel (which also forms D) + bwd_dkv_kernel, one pg_attn_bwd call"}
         L.close()
         del do, dq, dk, dv, delta
 

@@ -9,10 +9,11 @@
 // gradient of every response of its group. P is recomputed from Q, K and the
 // forward's lse, so no attention matrix is kept.
 //
-// Three launches:
-//  * bwd_delta_kernel: D for every (token, head) row.
+// Two launches:
 //  * bwd_dq_kernel: the forward's work items (query blocks x heads). Per wave
-//    32 query rows; per 64-key tile of the item's key spans
+//    32 query rows. Its prologue works out D of each row from the dO row it
+//    loads anyway and writes it out for the next launch. Then per 64-key tile
+//    of the item's key spans
 //      S^T = K Q^T, dP^T = V dO^T           (A = K, V rows from LDS)
 //      P^T = exp2(S^T c - lse2), dS^T = P^T (dP^T - D)
 //      dQ^T += K^T dS^T                     (A = K^T by transposing LDS reads,
@@ -116,33 +117,6 @@ __device__ inline void store_tile(const f32x16_t* acc, float mul, unsigned char*
   }
 }
 
-// ------------------------------------------------------------------- delta --
-
-// D[h][t] = sum_d dO[t,h,d] O[t,h,d] in fp32; 16 lanes per (t, h) row.
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const uint16_t* dout,
-                                                        float* delta, int T, int Hq) {
-  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);   // t * Hq + h
-  const int sub = threadIdx.x & 15;
-  const int64_t rows = int64_t(T) * Hq;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint4 a = ldg16(o + row * D + 8 * sub);
-    const uint4 b = ldg16(dout + row * D + 8 * sub);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x = (&a.x)[j], y = (&b.x)[j];
-      acc = fmaf(bf16_lo(x), bf16_lo(y), acc);
-      acc = fmaf(bf16_hi(x), bf16_hi(y), acc);
-    }
-  }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (sub == 0 && row < rows) {
-    const int64_t t = row / Hq, h = row % Hq;
-    delta[h * T + t] = acc;
-  }
-}
-
 // ---------------------------------------------------------------------- dQ --
 
 constexpr int Q_KT = PG_KEY_TILE;            // 64 keys per tile
@@ -158,8 +132,9 @@ struct BwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
+  const uint16_t* o;
   const float* lse;
-  const float* delta;
+  float* delta;   // written by the dQ launch, read by the dK/dV launch
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -221,7 +196,25 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
   float lse2 = a.lse[int64_t(h) * a.T + tq] * LOG2E;
-  float dlt = a.delta[int64_t(h) * a.T + tq];
+  // D = sum_d dO O of this row in fp32: each half of the wave holds half of d.
+  // The items cover every (token, head) row once, so D is complete for the
+  // dK/dV launch that follows.
+  float dlt = 0.f;
+  {
+    const int64_t base = (int64_t(tq) * a.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 x = ldg16(a.o + base + 16 * ks);
+      const uint4 y = __builtin_bit_cast(uint4, dof[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dlt = fmaf(bf16_lo((&x.x)[j]), bf16_lo((&y.x)[j]), dlt);
+        dlt = fmaf(bf16_hi((&x.x)[j]), bf16_hi((&y.x)[j]), dlt);
+      }
+    }
+    dlt += other_half(dlt);
+    if (row_valid && half == 0) a.delta[int64_t(h) * a.T + tq] = dlt;
+  }
   int ss_t = a.tok_ss[tq];
   // Redefine the loaded values by an empty asm: the compiler waits for their
   // loads once, here. Counted inside the tile loop instead, next to the tile
@@ -640,10 +633,8 @@ hipError_t pg_launch_attn_bwd(const pg_layout& L, const void* q, const void* k, 
                               void* dk, void* dv, float* delta, float softmax_scale,
                               hipStream_t stream) {
   if (L.items.empty()) return hipSuccess;
-  const int64_t rows = L.T * L.Hq;
-  bwd_delta_kernel<<<dim3(uint32_t((rows + 15) / 16)), dim3(256), 0, stream>>>(
-      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), delta, int(L.T), L.Hq);
   BwdArgs a;
+  a.o = static_cast<const uint16_t*>(o);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
