@@ -60,17 +60,19 @@ def test_pack_unpack_edge_shapes(case):
         _check(w, tail, dtype, seed=100 + case)
 
 
-def test_gathers_larger_than_the_last_level_cache():
-    """Hidden-state rows (4 KB) on the GRPO-shaped workload: every gather
+@pytest.mark.parametrize("row", [4096, 4100])
+def test_gathers_larger_than_the_last_level_cache(row):
+    """Hidden-state-sized rows on the GRPO-shaped workload: every gather
     writes more than 256 MB, so the kernels take their streaming-store branch
-    (the cases above, all smaller, take the ordinary one)."""
+    (the cases above, all smaller, take the ordinary one). 4096-byte rows move
+    in 16-byte units, 4100-byte rows in 4-byte units."""
     w = make_workload(2)
     lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
     G, N, T = len(w.prefix_lens), len(w.suffix_lens), int(w.total_tokens)
-    ppad, spad, row = int(w.prefix_lens.max()), int(w.suffix_lens.max()), 4096
+    ppad, spad = int(w.prefix_lens.max()), int(w.suffix_lens.max())
     assert T * row > 256 << 20
     print(f"large gathers: {w.name} T={T}, {row}-byte rows", flush=True)
-    r = np.random.default_rng(77)
+    r = np.random.default_rng(77 + row)
     prefix = r.integers(0, 256, size=(G, ppad, row), dtype=np.uint8)
     suffix = r.integers(0, 256, size=(N, spad, row), dtype=np.uint8)
     L = pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
