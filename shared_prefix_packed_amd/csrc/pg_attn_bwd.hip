@@ -196,25 +196,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
   float lse2 = a.lse[int64_t(h) * a.T + tq] * LOG2E;
-  // D = sum_d dO O of this row in fp32: each half of the wave holds half of d.
-  // The items cover every (token, head) row once, so D is complete for the
-  // dK/dV launch that follows.
   float dlt = 0.f;
-  {
-    const int64_t base = (int64_t(tq) * a.Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 x = ldg16(a.o + base + 16 * ks);
-      const uint4 y = __builtin_bit_cast(uint4, dof[ks]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dlt = fmaf(bf16_lo((&x.x)[j]), bf16_lo((&y.x)[j]), dlt);
-        dlt = fmaf(bf16_hi((&x.x)[j]), bf16_hi((&y.x)[j]), dlt);
-      }
-    }
-    dlt += other_half(dlt);
-    if (row_valid && half == 0) a.delta[int64_t(h) * a.T + tq] = dlt;
-  }
   int ss_t = a.tok_ss[tq];
   // Redefine the loaded values by an empty asm: the compiler waits for their
   // loads once, here. Counted inside the tile loop instead, next to the tile
@@ -270,6 +252,26 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
     ld.next(a.spans);
   }
   cp.init(a.spans, it.span0, it.nspan);
+  // D = sum_d dO O of this row in fp32: each half of the wave holds half of d.
+  // The items cover every (token, head) row once, so D is complete for the
+  // dK/dV launch that follows. Formed after the first tile fetches are issued,
+  // so that the O loads overlap them.
+  {
+    const int64_t base = (int64_t(tq) * a.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 x = ldg16(a.o + base + 16 * ks);
+      const uint4 y = __builtin_bit_cast(uint4, dof[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dlt = fmaf(bf16_lo((&x.x)[j]), bf16_lo((&y.x)[j]), dlt);
+        dlt = fmaf(bf16_hi((&x.x)[j]), bf16_hi((&y.x)[j]), dlt);
+      }
+    }
+    dlt += other_half(dlt);
+    if (row_valid && half == 0) a.delta[int64_t(h) * a.T + tq] = dlt;
+  }
+  asm volatile("" : "+v"(dlt));
 
   // Waves 0-3 take each tile whole in its iteration; waves 4-7 run half a tile
   // behind: first P, dS and the dQ product of the previous tile, then S and dP
