@@ -476,6 +476,9 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
   // B operands of the first product, rows of the slice's keys (lane: key col,
   // d = 16 ks + 8 half + 0..7; keys past the block are zero): K for S = Q K^T
   // (dV role), V for dP = dO V^T (dK role)
+  // The first tile is fetched while these registers load; the second after
+  // their wait, which would otherwise drain it as well.
+  kv_fetch(a, c, 0, 0);
   bf16x8_t bf[8];
   {
     const bool key_valid = c.key < c.kw1;
@@ -501,7 +504,6 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  kv_fetch(a, c, 0, 0);
   if (c.ntiles > 1) kv_fetch(a, c, 1, 1);
 
   for (int n = 0; n < c.ntiles; ++n) {
