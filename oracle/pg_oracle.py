@@ -482,6 +482,44 @@ def attention_backward(q, k, v, do, lay, scale: float, num_q_heads: int,
     return dq, dk, dv
 
 
+def attention_backward_dq_rows(q, k, v, do, lay, scale: float, num_q_heads: int,
+                               num_kv_heads: int, tokens: Sequence[int],
+                               heads: Sequence[int]) -> np.ndarray:
+    """Selected rows of dQ by the same chain rule as ``attention_backward``,
+    one (token, head) at a time over that row's key set (the keys of
+    ``attention_rows``): with p the row's softmax over its keys,
+      o = p V,  D = dO . o,  dp_j = dO . v_j,  dq = scale * sum_j p_j (dp_j - D) k_j.
+    A query row's dQ needs only its own row of P, so this is cheap at full size.
+    Returns [n, d] in fp64 for the pairs zip(tokens, heads). Pinned by:
+    equality with ``attention_backward`` on every row of small workloads;
+    closed forms (constant V gives dq = 0; a row with one key has dq = 0)."""
+    T, Hq, d = q.shape
+    bounds = {}
+    for g, p0, P, (s0, s1) in sequences(lay):
+        for t in range(s0, s1):
+            bounds[t] = (p0, P, s0)
+    out = np.zeros((len(tokens), d))
+    for n, (t, h) in enumerate(zip(tokens, heads)):
+        t, h = int(t), int(h)
+        hk = _kv_head(h, Hq, num_kv_heads)
+        if t in bounds:
+            p0, P, s0 = bounds[t]
+            keys = np.concatenate([np.arange(p0, p0 + P), np.arange(s0, t + 1)])
+        else:  # prompt token
+            keys = np.arange(int(lay["g0"][t]), t + 1)
+        qq = np.asarray(q[t, h], dtype=np.float64)
+        gg = np.asarray(do[t, h], dtype=np.float64)
+        kk = np.asarray(k[keys, hk], dtype=np.float64)
+        vv = np.asarray(v[keys, hk], dtype=np.float64)
+        s = scale * (kk @ qq)
+        e = np.exp(s - s.max())
+        p = e / e.sum()
+        D = gg @ (p @ vv)
+        dp = vv @ gg
+        out[n] = scale * ((p * (dp - D)) @ kk)
+    return out
+
+
 def backward_flop(lay, head_dim: int, num_q_heads: int) -> int:
     """Algorithmic FLOP of the backward: five products over the allowed pairs
     (S = QK^T recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q),

@@ -138,6 +138,45 @@ def test_backward_long_prefix_properties():
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
 
 
+class _Bf16Rows:
+    """bf16 bit array read as float32 only where indexed (the oracle's per-row
+    functions touch a few rows of tensors too large to widen whole)."""
+
+    def __init__(self, bits):
+        self.bits = bits
+        self.shape = bits.shape
+
+    def __getitem__(self, idx):
+        return bf16_bits_to_f32(self.bits[idx])
+
+
+def test_backward_long_prefix_sampled_dq_rows():
+    """dQ rows at the long-prefix size against the oracle's per-row chain rule:
+    prompt rows with up to 16K keys, response rows, every group's first and
+    last prompt token and every response's last token, on random heads."""
+    w = make_workload(4)
+    x, dq, dk, dv, L = run_gpu(w)
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    r = np.random.default_rng(404)
+    go = np.asarray(lay["group_off"])
+    picks = [w.total_tokens - 1]
+    for g in range(len(w.prefix_lens)):
+        picks += [int(go[g]), int(go[g]) + int(w.prefix_lens[g]) - 1]
+    picks += [int(t) for t in r.integers(0, w.total_tokens, size=16)]
+    picks += [int(t) for t in np.nonzero(np.diff(np.asarray(lay["ss"])) != 0)[0]]   # last row of each segment
+    tokens = sorted(set(picks))
+    heads = [int(h) for h in r.integers(0, w.num_q_heads, size=len(tokens))]
+    say(f"backward: workload {w.name} T={w.total_tokens}, {len(tokens)} sampled dQ rows")
+    f = {n: _Bf16Rows(x[n]) for n in ("q", "k", "v", "do")}
+    want = O.attention_backward_dq_rows(f["q"], f["k"], f["v"], f["do"], lay, w.softmax_scale,
+                                        w.num_q_heads, w.num_kv_heads, tokens, heads)
+    got = dq[tokens, heads]
+    scale = max(1.0, np.abs(want).max())
+    assert np.abs(got - want).max() <= ABS_TOL * scale, np.abs(got - want).max()
+    assert np.linalg.norm(got - want) <= REL_TOL * np.linalg.norm(want)
+    L.close()
+
+
 def test_backward_deterministic_and_fully_written():
     w = make_workload(1)
     x = {n: draw_tensor(w, n) for n in ("q", "k", "v", "do")}

@@ -122,6 +122,40 @@ def test_backward_closed_forms():
     assert np.abs(dq2).max() < 1e-12 and np.abs(dk2).max() < 1e-12
 
 
+@pytest.mark.parametrize("case", CASES + [([6, 3], [[4, 0, 5], [2, 3]], 8, 2, 16)])
+def test_dq_rows_equal_the_dense_backward(case):
+    """The per-row dQ (used at full size) equals the dense per-group backward,
+    which finite differences and torch autograd pin, on every (token, head)."""
+    P, S, hq, hkv, d = case
+    w, lay, q, k, v, do = _inputs(P, S, hq, hkv, d, seed=11)
+    dq, _, _ = O.attention_backward(q, k, v, do, lay, w.softmax_scale, hq, hkv)
+    T = q.shape[0]
+    tokens = np.repeat(np.arange(T), hq)
+    heads = np.tile(np.arange(hq), T)
+    rows = O.attention_backward_dq_rows(q, k, v, do, lay, w.softmax_scale, hq, hkv, tokens, heads)
+    assert np.abs(rows - dq[tokens, heads]).max() <= 1e-12 * max(1.0, np.abs(dq).max())
+
+
+def test_dq_rows_closed_forms():
+    w, lay, q, k, v, do = _inputs([5, 2], [[3, 4], [1, 2]], 4, 2, 8, seed=6)
+    T, hq = q.shape[0], w.num_q_heads
+    tokens = np.repeat(np.arange(T), hq)
+    heads = np.tile(np.arange(hq), T)
+    # the same V for every key: the output does not depend on the scores
+    vc = np.broadcast_to(v[:1], v.shape).copy()
+    rows = O.attention_backward_dq_rows(q, k, vc, do, lay, w.softmax_scale, hq, w.num_kv_heads,
+                                        tokens, heads)
+    assert np.abs(rows).max() < 1e-12
+    # a group's first token has one key: P = 1, so dS = dp - D = 0
+    firsts = [int(lay["group_off"][g]) for g in range(2)]
+    rows = O.attention_backward_dq_rows(q, k, v, do, lay, w.softmax_scale, hq, w.num_kv_heads,
+                                        [t for t in firsts for _ in range(hq)], list(range(hq)) * 2)
+    assert np.abs(rows).max() < 1e-12
+    # a row with several keys does get a gradient
+    last = O.attention_backward_dq_rows(q, k, v, do, lay, w.softmax_scale, hq, w.num_kv_heads, [T - 1], [0])
+    assert np.abs(last).max() > 1e-3
+
+
 def test_finite_differences_catch_a_dropped_term():
     """A plausible mistake (dS = P dP, the D term dropped) fails the pin."""
     w, lay, q, k, v, do = _inputs(*CASES[0])
