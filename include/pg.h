@@ -316,7 +316,8 @@ pg_status pg_unpack_rows(const pg_layout* layout, const void* packed, int64_t ro
  *  dout        dO [T, Hq, d]
  *  dq          [T, Hq, d], dk, dv [T, Hkv, d]: written completely (every row of
  *              dk/dv is written, zero where no query reads the key)
- *  delta       caller-owned device scratch of Hq * T floats (D per row)
+ *  delta       caller-owned device scratch of Hq * T floats; on return it holds
+ *              D = rowsum(dO * O) of every (head, token) row, fp32 [Hq, T]
  * All tensors share dtype; PG_ERR_UNSUPPORTED unless dtype == PG_BF16 and
  * d == 128. dq, dk, dv must not alias the inputs or each other.
  */
