@@ -138,6 +138,37 @@ def test_backward_long_prefix_properties():
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
 
 
+def test_backward_returns_d_in_delta():
+    """delta holds D = rowsum(dO * O) of every (head, token) row on return.
+    The GPU forms D from its bf16 O, whose error against the fp64 O is at
+    most 2^-9 |O_d| (rounding to bf16) plus 2^-9 sum_j p_j |v_jd| (P rounded
+    to bf16 before the PV product; that sum is attention over |V|), so per row
+      |D_gpu - D_ref| <= 2^-8 sum_d |dO_d| (|O_d| + sum_j p_j |v_jd|) + 1e-5,
+    and over all rows the relative l2 error stays within the module's 2 %."""
+    w = make_workload(1)
+    x = {n: draw_tensor(w, n) for n in ("q", "k", "v", "do")}
+    L = pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
+                           w.num_kv_heads, w.head_dim, w.rope_theta)
+    q, k, v, do = (dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+    delta = torch.full((w.num_q_heads, w.total_tokens), float("nan"), dtype=torch.float32, device="cuda")
+    pg.pg_attn_bwd(L, q, k, v, o, lse, do, w.softmax_scale, delta=delta)
+    torch.cuda.synchronize()
+    got = delta.cpu().numpy().astype(np.float64)
+    f = {n: bf16_bits_to_f32(x[n]).astype(np.float64) for n in ("q", "k", "v", "do")}
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    o_ref, _ = O.attention(f["q"], f["k"], f["v"], lay, w.softmax_scale, w.num_q_heads, w.num_kv_heads)
+    want = (f["do"] * o_ref).sum(axis=2).T                                  # [Hq, T]
+    o_abs, _ = O.attention(f["q"], f["k"], np.abs(f["v"]), lay, w.softmax_scale, w.num_q_heads,
+                           w.num_kv_heads)                                 # sum_j p_j |v_j|
+    bound = 2.0 ** -8 * (np.abs(f["do"]) * (np.abs(o_ref) + o_abs)).sum(axis=2).T + 1e-5
+    say(f"delta: {w.name}, worst |D_gpu - D_ref| / bound = {(np.abs(got - want) / bound).max():.3f}")
+    assert np.isfinite(got).all()
+    assert (np.abs(got - want) <= bound).all()
+    assert np.linalg.norm(got - want) <= REL_TOL * np.linalg.norm(want)
+    L.close()
+
+
 class _Bf16Rows:
     """bf16 bit array read as float32 only where indexed (the oracle's per-row
     functions touch a few rows of tensors too large to widen whole)."""
