@@ -135,29 +135,23 @@ def sequences(lay) -> Iterable[Tuple[int, int, int, int]]:
 def positions(lay) -> np.ndarray:
     """int64 position id per packed token.
 
-    verl page, section 1 (building position ids): within a group the prompt
-    takes 0..P-1; every non-empty response takes P..P+S-1, written right after
-    the previous one; empty responses consume nothing. Written here as that
-    loop over groups and responses, on the unpadded packed row.
+    verl page, section 1 (building position ids) and the prefix-sharing
+    diagram: every response continues the prompt independently, as if
+    prompt || response were its own sequence, so a token's position is its
+    index in that unpacked sequence. In terms of the layout's per-token
+    descriptors (g0 = group start, pe = prompt end, ss = own segment start):
+    a prompt token t has position t - g0; a response token has the prompt
+    length pe - g0 plus its index t - ss in its own response.
 
     Pinned by: hand-derived ids of the tiny workload; equality with
     arange(P+S) of each unpacked sequence.
     """
     T = int(lay["total_tokens"])
-    pos = np.zeros(T, dtype=np.int64)
-    k = 0
-    for g in range(len(lay["prefix_lens"])):
-        base = int(lay["group_off"][g])
-        P = int(lay["prefix_lens"][g])
-        pos[base:base + P] = np.arange(P)
-        cur = base + P
-        for _ in range(int(lay["suffix_counts"][g])):
-            s = int(lay["suffix_lens"][k])
-            k += 1
-            if s > 0:
-                pos[cur:cur + s] = np.arange(P, P + s)
-                cur += s
-    return pos
+    t = np.arange(T, dtype=np.int64)
+    g0 = np.asarray(lay["g0"], dtype=np.int64)
+    pe = np.asarray(lay["pe"], dtype=np.int64)
+    ss = np.asarray(lay["ss"], dtype=np.int64)
+    return np.where(t < pe, t - g0, (pe - g0) + (t - ss)).astype(np.int64)
 
 
 # -------------------------------------------------------------------- rope --
@@ -427,7 +421,8 @@ def group_mask(lay, g: int) -> np.ndarray:
 
 
 def attention_backward(q, k, v, do, lay, scale: float, num_q_heads: int,
-                       num_kv_heads: int, groups: Sequence[int] = None):
+                       num_kv_heads: int, groups: Sequence[int] = None,
+                       magnitudes: bool = False):
     """Gradients of the packed attention output, by the chain rule.
 
     The packed forward (``attention``) maps Q, K, V to O with one softmax per
@@ -449,6 +444,14 @@ def attention_backward(q, k, v, do, lay, scale: float, num_q_heads: int,
     torch's float64 SDPA autograd on the unpacked sequences (library routine);
     closed forms (constant V gives dQ = dK = 0; the keys' dV sum to the
     queries' dO sum; a group's first token has dQ = 0).
+
+    With ``magnitudes`` it also returns, per output element, the root sum of
+    squares of the terms of its defining sum (what a probabilistic rounding
+    error bound scales with; not part of the gradient): for dV_j the terms
+    p_ij dO_i, for dK_j the terms scale (|dS_ij| + p_ij delta_i) q_i and for
+    dQ_i the terms scale (|dS_ij| + p_ij delta_i) k_j, where delta_i =
+    ||dO_i * O_i||_2 is the size of the products D_i sums. Returned as a
+    fourth item {"dq", "dk", "dv"} of arrays shaped like the gradients.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -458,6 +461,10 @@ def attention_backward(q, k, v, do, lay, scale: float, num_q_heads: int,
     dq = np.zeros_like(q)
     dk = np.zeros(k.shape, dtype=np.float64)
     dv = np.zeros(v.shape, dtype=np.float64)
+    if magnitudes:
+        mq = np.zeros_like(dq)
+        mk = np.zeros_like(dk)
+        mv = np.zeros_like(dv)
     if groups is None:
         groups = range(len(lay["prefix_lens"]))
     for g in groups:
@@ -479,12 +486,20 @@ def attention_backward(q, k, v, do, lay, scale: float, num_q_heads: int,
             dq[a:b, h] = scale * (dS @ K)
             dk[a:b, hk] += scale * (dS.T @ Q)
             dv[a:b, hk] += P.T @ dO
+            if magnitudes:
+                delta = np.sqrt(((dO * O) ** 2).sum(axis=1, keepdims=True))
+                A2 = (np.abs(dS) + P * delta) ** 2
+                mq[a:b, h] = scale ** 2 * (A2 @ (K * K))
+                mk[a:b, hk] += scale ** 2 * (A2.T @ (Q * Q))
+                mv[a:b, hk] += (P * P).T @ (dO * dO)
+    if magnitudes:
+        return dq, dk, dv, {"dq": np.sqrt(mq), "dk": np.sqrt(mk), "dv": np.sqrt(mv)}
     return dq, dk, dv
 
 
 def attention_backward_dq_rows(q, k, v, do, lay, scale: float, num_q_heads: int,
                                num_kv_heads: int, tokens: Sequence[int],
-                               heads: Sequence[int]) -> np.ndarray:
+                               heads: Sequence[int], magnitudes: bool = False):
     """Selected rows of dQ by the same chain rule as ``attention_backward``,
     one (token, head) at a time over that row's key set (the keys of
     ``attention_rows``): with p the row's softmax over its keys,
@@ -492,13 +507,17 @@ def attention_backward_dq_rows(q, k, v, do, lay, scale: float, num_q_heads: int,
     A query row's dQ needs only its own row of P, so this is cheap at full size.
     Returns [n, d] in fp64 for the pairs zip(tokens, heads). Pinned by:
     equality with ``attention_backward`` on every row of small workloads;
-    closed forms (constant V gives dq = 0; a row with one key has dq = 0)."""
+    closed forms (constant V gives dq = 0; a row with one key has dq = 0).
+    With ``magnitudes`` it also returns the root sum of squares of the terms
+    scale (|dS_j| + p_j delta) k_j per element, delta = ||dO * o||_2, as
+    ``attention_backward`` defines them."""
     T, Hq, d = q.shape
     bounds = {}
     for g, p0, P, (s0, s1) in sequences(lay):
         for t in range(s0, s1):
             bounds[t] = (p0, P, s0)
     out = np.zeros((len(tokens), d))
+    mag = np.zeros((len(tokens), d))
     for n, (t, h) in enumerate(zip(tokens, heads)):
         t, h = int(t), int(h)
         hk = _kv_head(h, Hq, num_kv_heads)
@@ -514,10 +533,83 @@ def attention_backward_dq_rows(q, k, v, do, lay, scale: float, num_q_heads: int,
         s = scale * (kk @ qq)
         e = np.exp(s - s.max())
         p = e / e.sum()
-        D = gg @ (p @ vv)
+        o = p @ vv
+        D = gg @ o
         dp = vv @ gg
-        out[n] = scale * ((p * (dp - D)) @ kk)
+        dS = p * (dp - D)
+        out[n] = scale * (dS @ kk)
+        if magnitudes:
+            delta = math.sqrt(float(((gg * o) ** 2).sum()))
+            mag[n] = scale * np.sqrt(((np.abs(dS) + p * delta) ** 2) @ (kk * kk))
+    if magnitudes:
+        return out, mag
     return out
+
+
+def attention_backward_kv_rows(q, k, v, do, lay, scale: float, num_q_heads: int,
+                               num_kv_heads: int, keys: Sequence[int],
+                               kv_heads: Sequence[int], o=None, lse=None,
+                               magnitudes: bool = False):
+    """Selected rows of dK and dV by the same chain rule as
+    ``attention_backward``, one (key token, KV head) at a time, summed over
+    the query rows that read the key.
+
+    Query token t reads key j iff j is in K(t) (``allowed_keys``): every later
+    token of the group for a prompt key (the rest of the prompt and every
+    response: "Preference Packing", core idea, the prompt is shared by all
+    responses, so its gradient collects all of them), the rest of its own
+    response for a response key. For each such t and each query head h of the
+    KV head, with the row's own softmax p_tj = exp(scale q_t.k_j - lse_t) and
+    D_t = dO_t . o_t:
+      dV_j += p_tj dO_t,   dK_j += scale p_tj (dO_t . v_j - D_t) q_t.
+    ``o`` [T, Hq, d] and ``lse`` [Hq, T] are the forward's output and
+    logsumexp from ``attention`` (computed here over every row when not given;
+    then only for small layouts); only the rows of the groups of the selected
+    keys and the query heads of the selected KV heads are read.
+    Returns (dk [n, d], dv [n, d]) for the pairs zip(keys, kv_heads), and with
+    ``magnitudes`` also the root sum of squares of their terms as
+    ``attention_backward`` defines them: (dk, dv, mag_dk, mag_dv).
+    Pinned by: equality with ``attention_backward`` on every key row of small
+    layouts; closed forms (constant V gives dk = 0; over a group's keys dV sums
+    to the group's dO and dK to zero).
+    """
+    T, Hq, d = q.shape
+    r = Hq // num_kv_heads
+    if o is None or lse is None:
+        o, lse = attention(q, k, v, lay, scale, num_q_heads, num_kv_heads)
+    go = np.asarray(lay["group_off"], dtype=np.int64)
+    ss_all = np.asarray(lay["ss"], dtype=np.int64)
+    n = len(keys)
+    dk = np.zeros((n, d))
+    dv = np.zeros((n, d))
+    mk = np.zeros((n, d))
+    mv = np.zeros((n, d))
+    for idx, (j, hk) in enumerate(zip(keys, kv_heads)):
+        j, hk = int(j), int(hk)
+        g0, pe = int(lay["g0"][j]), int(lay["pe"][j])
+        g = int(np.searchsorted(go, g0, side="right")) - 1
+        gend = int(go[g + 1])
+        t = np.arange(j, gend)
+        if j >= pe:   # response key: only the rest of its own response reads it
+            t = t[ss_all[j:gend] == ss_all[j]]
+        kj = np.asarray(k[j, hk], dtype=np.float64)
+        vj = np.asarray(v[j, hk], dtype=np.float64)
+        for h in range(hk * r, (hk + 1) * r):
+            qt = np.asarray(q[t, h], dtype=np.float64)
+            gt = np.asarray(do[t, h], dtype=np.float64)
+            ot = np.asarray(o[t, h], dtype=np.float64)
+            p = np.exp(scale * (qt @ kj) - np.asarray(lse[h, t], dtype=np.float64))
+            D = (gt * ot).sum(axis=1)
+            dS = p * (gt @ vj - D)
+            dv[idx] += p @ gt
+            dk[idx] += scale * (dS @ qt)
+            if magnitudes:
+                delta = np.sqrt(((gt * ot) ** 2).sum(axis=1))
+                mv[idx] += (p * p) @ (gt * gt)
+                mk[idx] += scale ** 2 * (((np.abs(dS) + p * delta) ** 2) @ (qt * qt))
+    if magnitudes:
+        return dk, dv, np.sqrt(mk), np.sqrt(mv)
+    return dk, dv
 
 
 def backward_flop(lay, head_dim: int, num_q_heads: int) -> int:
@@ -599,25 +691,19 @@ def group_lens(lay) -> np.ndarray:
 def padded_positions(lay, max_len: int) -> np.ndarray:
     """Position ids of the right-padded form [G, max_len].
 
-    verl page, section 1 (building position ids): a zero-filled int64 tensor;
-    row g holds its prompt's positions 0..P-1, then every non-empty response's
-    P..P+S-1 in order; padding stays 0. Written out by that loop.
+    verl page, section 1 (building position ids): the padded tensor starts
+    zero-filled and row g holds group g's packed row, so its first n_g entries
+    are the packed positions of the group's tokens (``positions``) and the
+    right padding keeps 0.
     Pinned by: hand-derived rows of the tiny workload; real tokens equal
     ``positions`` (the packed form).
     """
     G = len(lay["prefix_lens"])
     out = np.zeros((G, max_len), dtype=np.int64)
-    k = 0
+    pos = positions(lay)
+    go = np.asarray(lay["group_off"], dtype=np.int64)
     for g in range(G):
-        P = int(lay["prefix_lens"][g])
-        out[g, :P] = np.arange(P)
-        cur = P
-        for _ in range(int(lay["suffix_counts"][g])):
-            S = int(lay["suffix_lens"][k])
-            k += 1
-            if S > 0:
-                out[g, cur:cur + S] = np.arange(P, P + S)
-                cur += S
+        out[g, :go[g + 1] - go[g]] = pos[go[g]:go[g + 1]]
     return out
 
 

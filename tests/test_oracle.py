@@ -200,6 +200,38 @@ def test_rope_d2_is_plain_rotation_matrix():
     assert np.abs(y - R @ x[0, 0]).max() <= 1e-15
 
 
+def test_rope_frequency_schedule_hand_derived():
+    """The frequency schedule omega_i = theta^(-2i/d), pinned by values worked
+    out by hand (no program): with d = 8 and theta = 1e4 the four pairs turn at
+    1, 1e4^(-1/4) = 0.1, 1e4^(-1/2) = 0.01 and 1e4^(-3/4) = 0.001 rad per
+    position; with d = 4 at 1 and 0.01; with d = 128 and theta = 5e5 pair 32
+    turns at 5e5^(-1/2) = sqrt(2)/1000. Pair i is (x_i, x_{i+d/2}). A schedule
+    theta^(-i/d), an interleaved pairing (x_2i, x_2i+1) or a turn by -phi all
+    move some output below by far more than the 1e-12 allowed."""
+    def rotated(lo, hi, a):
+        return lo * math.cos(a) - hi * math.sin(a), hi * math.cos(a) + lo * math.sin(a)
+
+    # d = 8, theta = 1e4, position 3: angles 3, 0.3, 0.03, 0.003
+    x = np.array([[[1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0, 8.0]]])
+    y = O.rope(x, np.array([3]), 1e4)[0, 0]
+    for i, a in enumerate([3.0, 0.3, 0.03, 0.003]):
+        want = rotated(x[0, 0, i], x[0, 0, i + 4], a)
+        assert abs(y[i] - want[0]) <= 1e-12 and abs(y[i + 4] - want[1]) <= 1e-12
+    # d = 4, theta = 1e4, position 100: angles 100 and 1
+    x = np.array([[[0.5, -1.5, 2.0, 0.25]]])
+    y = O.rope(x, np.array([100]), 1e4)[0, 0]
+    for i, a in enumerate([100.0, 1.0]):
+        want = rotated(x[0, 0, i], x[0, 0, i + 2], a)
+        assert abs(y[i] - want[0]) <= 1e-12 and abs(y[i + 2] - want[1]) <= 1e-12
+    # d = 128, theta = 5e5, position 1000: pair 0 turns by 1000 rad, pair 32 by sqrt(2)
+    x = np.zeros((1, 1, 128))
+    x[0, 0, 0], x[0, 0, 64], x[0, 0, 32], x[0, 0, 96] = 1.0, 0.0, 1.0, 0.0
+    y = O.rope(x, np.array([1000]), 5e5)[0, 0]
+    assert abs(y[0] - math.cos(1000.0)) <= 1e-12 and abs(y[64] - math.sin(1000.0)) <= 1e-12
+    assert abs(y[32] - math.cos(math.sqrt(2.0))) <= 1e-12
+    assert abs(y[96] - math.sin(math.sqrt(2.0))) <= 1e-12
+
+
 def test_rope_keeps_pair_norms_and_is_relative():
     r = np.random.default_rng(2)
     q = r.standard_normal((1, 1, 32))

@@ -156,6 +156,77 @@ def test_dq_rows_closed_forms():
     assert np.abs(last).max() > 1e-3
 
 
+@pytest.mark.parametrize("case", CASES + [([6, 3], [[4, 0, 5], [2, 3]], 8, 2, 16)])
+def test_kv_rows_equal_the_dense_backward(case):
+    """The per-key dK/dV (used at full size, where a prompt key is read by
+    every response of its group) equals the dense per-group backward, which
+    finite differences and torch autograd pin, on every (key, KV head)."""
+    P, S, hq, hkv, d = case
+    w, lay, q, k, v, do = _inputs(P, S, hq, hkv, d, seed=12)
+    _, dk, dv = O.attention_backward(q, k, v, do, lay, w.softmax_scale, hq, hkv)
+    T = q.shape[0]
+    keys = np.repeat(np.arange(T), hkv)
+    kvh = np.tile(np.arange(hkv), T)
+    rk, rv = O.attention_backward_kv_rows(q, k, v, do, lay, w.softmax_scale, hq, hkv, keys, kvh)
+    tol = 1e-12 * max(1.0, np.abs(dk).max(), np.abs(dv).max())
+    assert np.abs(rk - dk[keys, kvh]).max() <= tol
+    assert np.abs(rv - dv[keys, kvh]).max() <= tol
+    # the forward's o and lse handed in give the same rows
+    o, lse = O.attention(q, k, v, lay, w.softmax_scale, hq, hkv)
+    rk2, rv2 = O.attention_backward_kv_rows(q, k, v, do, lay, w.softmax_scale, hq, hkv, keys, kvh,
+                                            o=o, lse=lse)
+    assert np.array_equal(rk, rk2) and np.array_equal(rv, rv2)
+
+
+def test_kv_rows_closed_forms():
+    w, lay, q, k, v, do = _inputs([5, 2], [[3, 4], [1, 2]], 4, 2, 8, seed=7)
+    T, hq, hkv = q.shape[0], w.num_q_heads, w.num_kv_heads
+    r = hq // hkv
+    keys = np.repeat(np.arange(T), hkv)
+    kvh = np.tile(np.arange(hkv), T)
+    dk, dv = O.attention_backward_kv_rows(q, k, v, do, lay, w.softmax_scale, hq, hkv, keys, kvh)
+    dk = dk.reshape(T, hkv, -1)
+    dv = dv.reshape(T, hkv, -1)
+    for g in range(2):
+        a, b = int(lay["group_off"][g]), int(lay["group_off"][g + 1])
+        for hk in range(hkv):
+            # rows of P sum to one: over a group's keys dV sums to its dO
+            assert np.allclose(dv[a:b, hk].sum(axis=0), do[a:b, hk * r:(hk + 1) * r].sum(axis=(0, 1)),
+                               atol=1e-12)
+            # rows of dS sum to zero: over a group's keys dK sums to zero
+            assert np.abs(dk[a:b, hk].sum(axis=0)).max() < 1e-12
+    # the same V for every key: no gradient reaches K
+    vc = np.broadcast_to(v[:1], v.shape).copy()
+    dk2, _ = O.attention_backward_kv_rows(q, k, vc, do, lay, w.softmax_scale, hq, hkv, keys, kvh)
+    assert np.abs(dk2).max() < 1e-12
+
+
+def test_backward_magnitudes_agree_across_forms():
+    """The per-element term magnitudes (root sum of squares of the terms of
+    each gradient sum, used to scale GPU tolerances) are the same in the dense
+    form and in the per-row forms, and bound each sum by Cauchy-Schwarz:
+    |sum of n terms| <= sqrt(n) * root sum of squares."""
+    P, S, hq, hkv, d = [6, 3], [[4, 0, 5], [2, 3]], 8, 2, 16
+    w, lay, q, k, v, do = _inputs(P, S, hq, hkv, d, seed=13)
+    dq, dk, dv, mags = O.attention_backward(q, k, v, do, lay, w.softmax_scale, hq, hkv, magnitudes=True)
+    T = q.shape[0]
+    tokens = np.repeat(np.arange(T), hq)
+    heads = np.tile(np.arange(hq), T)
+    _, mq = O.attention_backward_dq_rows(q, k, v, do, lay, w.softmax_scale, hq, hkv, tokens, heads,
+                                         magnitudes=True)
+    assert np.abs(mq - mags["dq"][tokens, heads]).max() <= 1e-12 * np.abs(mq).max()
+    keys = np.repeat(np.arange(T), hkv)
+    kvh = np.tile(np.arange(hkv), T)
+    _, _, mk, mv = O.attention_backward_kv_rows(q, k, v, do, lay, w.softmax_scale, hq, hkv, keys,
+                                                kvh, magnitudes=True)
+    assert np.abs(mk - mags["dk"][keys, kvh]).max() <= 1e-12 * np.abs(mk).max()
+    assert np.abs(mv - mags["dv"][keys, kvh]).max() <= 1e-12 * np.abs(mv).max()
+    n = T * hq   # more terms than any sum has
+    for g, m in ((dq, mags["dq"]), (dk, mags["dk"]), (dv, mags["dv"])):
+        assert (np.abs(g) <= np.sqrt(n) * m + 1e-12).all()
+        assert (m >= 0).all() and m.max() > 0
+
+
 def test_finite_differences_catch_a_dropped_term():
     """A plausible mistake (dS = P dP, the D term dropped) fails the pin."""
     w, lay, q, k, v, do = _inputs(*CASES[0])
