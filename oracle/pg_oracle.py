@@ -383,23 +383,27 @@ def attention_rows(q, k, v, lay, scale: float, num_q_heads: int,
             bounds[t] = (p0, P, s0)
     out_o = np.zeros((len(tokens), d))
     out_l = np.zeros(len(tokens))
+    # rows of one token and KV head share their key rows: gather them once
+    todo: Dict[Tuple[int, int], List[Tuple[int, int]]] = {}
     for n, (t, h) in enumerate(zip(tokens, heads)):
         t, h = int(t), int(h)
-        hk = _kv_head(h, Hq, num_kv_heads)
+        todo.setdefault((t, _kv_head(h, Hq, num_kv_heads)), []).append((n, h))
+    for (t, hk), rows in todo.items():
         if t in bounds:
             p0, P, s0 = bounds[t]
             keys = np.concatenate([np.arange(p0, p0 + P), np.arange(s0, t + 1)])
         else:  # prefix token
             g0 = int(lay["g0"][t])
             keys = np.arange(g0, t + 1)
-        qq = np.asarray(q[t, h], dtype=np.float64)
         kk = np.asarray(k[keys, hk], dtype=np.float64)
         vv = np.asarray(v[keys, hk], dtype=np.float64)
-        s = scale * (kk @ qq)
-        m = s.max()
-        p = np.exp(s - m)
-        out_o[n] = (p @ vv) / p.sum()
-        out_l[n] = m + math.log(p.sum())
+        for n, h in rows:
+            qq = np.asarray(q[t, h], dtype=np.float64)
+            s = scale * (kk @ qq)
+            m = s.max()
+            p = np.exp(s - m)
+            out_o[n] = (p @ vv) / p.sum()
+            out_l[n] = m + math.log(p.sum())
     return out_o, out_l
 
 

@@ -20,8 +20,11 @@ def _check(w, tail, dtype, seed):
     ppad = int(max(w.prefix_lens.max(initial=0), 0)) + 3
     spad = int(max(w.suffix_lens.max(initial=0), 0)) + 2
     r = np.random.default_rng(seed)
-    prefix = r.integers(-2**31, 2**31, size=(G, ppad) + tail).astype(dtype)
-    suffix = r.integers(-2**31, 2**31, size=(N, spad) + tail).astype(dtype)
+    # uniformly random bytes viewed as the row type, so every bit of every
+    # element varies (a gather moves bit patterns, NaN and inf included)
+    isz = np.dtype(dtype).itemsize
+    prefix = r.integers(0, 256, size=(G, ppad) + tail + (isz,), dtype=np.uint8).view(dtype)[..., 0]
+    suffix = r.integers(0, 256, size=(N, spad) + tail + (isz,), dtype=np.uint8).view(dtype)[..., 0]
     L = pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
                            w.num_kv_heads, w.head_dim, w.rope_theta)
     tp, ts = torch.from_numpy(prefix).cuda(), torch.from_numpy(suffix).cuda()

@@ -5,10 +5,14 @@ within 1 ulp of the storage dtype (bf16: count of 1-ulp differences reported
 and bounded; fp32: 1e-6 abs); attention output O max-abs error <= 2e-2 and
 lse error <= 1e-3, for fp32 and bf16.
 
-Small workloads are checked element by element against the full oracle; the
-full-size workloads on sampled (token, head) rows that the oracle computes one
-at a time by the definition (plus every group's first and last token and
-tile-boundary tokens), in the same launch configuration the benchmark times.
+The tiny, DPO, GRPO and heterogeneous workloads are checked on every row
+(the larger two with the oracle run per (group, query head) unit in parallel,
+tests/oracle_units.py); the long-prefix workload, whose oracle takes minutes,
+on sampled (token, head) rows that the oracle computes one at a time by the
+definition: every head of each segment's first and last tokens and of
+tile-boundary tokens, plus random rows. All in the same launch configuration
+the benchmark times, with O and lse filled with NaN before the launch, so an
+element the kernel leaves unwritten fails.
 """
 import math
 import sys
@@ -19,6 +23,7 @@ import torch
 
 import shared_prefix_packed_amd as pg
 from oracle import pg_oracle as O
+import oracle_units as U
 from workloads import bf16_bits_to_f32, draw_qkv, make_custom, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -69,15 +74,23 @@ def workload_inputs(i):
     return _cache[i]
 
 
-def sample_rows(lay, T, Hq, n, seed):
-    """Random (token, head) pairs plus structural edge tokens."""
+def sample_rows(lay, T, Hq, n, seed, all_heads_at_edges=False):
+    """Random (token, head) pairs plus structural edge tokens (segment starts
+    and ends, tile boundaries +-1). With all_heads_at_edges every head of each
+    edge token is taken; otherwise one random head per token."""
     r = np.random.default_rng(seed)
-    toks = list(r.integers(0, T, size=n))
+    edges = set()
     for a in lay["seg_off"]:
         for t in (a - 1, a, a + 1, a + 31, a + 32, a + 63, a + 64):
             if 0 <= t < T:
-                toks.append(int(t))
-    toks = sorted(set(int(t) for t in toks))
+                edges.add(int(t))
+    rand = [int(t) for t in r.integers(0, T, size=n)] if T else []
+    if all_heads_at_edges:
+        pairs = {(t, h) for t in edges for h in range(Hq)}
+        pairs |= {(t, int(h)) for t, h in zip(rand, r.integers(0, Hq, size=len(rand)))}
+        pairs = sorted(pairs)
+        return [t for t, _ in pairs], [h for _, h in pairs]
+    toks = sorted(edges | set(rand))
     heads = list(r.integers(0, Hq, size=len(toks)))
     # always include first and last head somewhere
     if toks:
@@ -86,25 +99,51 @@ def sample_rows(lay, T, Hq, n, seed):
     return toks, heads
 
 
+def poisoned_outputs(q, num_q_heads):
+    """O and lse filled with NaN, so any element the kernel does not write shows."""
+    T = q.shape[0]
+    return (torch.full_like(q, float("nan")),
+            torch.full((num_q_heads, T), float("nan"), dtype=torch.float32, device=q.device))
+
+
 def check_attn(w, o_gpu, lse_gpu, q, k, v, lay, full):
-    """Compare GPU (o, lse) with the oracle on all rows (full) or a sample."""
+    """Compare GPU (o, lse) with the oracle on every row or on a sample.
+
+    full=True: the whole oracle in one call (small workloads); "units": every
+    row, the oracle run per (group, query head) unit in parallel; False: the
+    sampled rows of ``sample_rows`` with every head at the edge tokens."""
     Hq = w.num_q_heads
     o_g = to_host_f32(o_gpu)
     l_g = lse_gpu.detach().cpu().numpy()
-    if full:
+    # every element written (the outputs were NaN-filled before the launch)
+    assert np.isfinite(o_g).all() and np.isfinite(l_g).all()
+    if full == "units":
+        eo, el, rows = U.max_errors(w, lay, q, k, v, o_g, l_g)
+        assert rows == w.total_tokens * Hq
+        what = f"all {rows} rows"
+    elif full:
         o_ref, l_ref = O.attention(q, k, v, lay, w.softmax_scale, Hq, w.num_kv_heads)
         eo = np.abs(o_g.astype(np.float64) - o_ref).max()
         el = np.abs(l_g.astype(np.float64) - l_ref).max()
+        what = f"all {w.total_tokens * Hq} rows"
     else:
-        toks, heads = sample_rows(lay, w.total_tokens, Hq, 300, 17 + max(w.index, 0))
+        toks, heads = sample_rows(lay, w.total_tokens, Hq, 1500, 17 + max(w.index, 0),
+                                  all_heads_at_edges=True)
         o_ref, l_ref = O.attention_rows(q, k, v, lay, w.softmax_scale, Hq, w.num_kv_heads,
                                         toks, heads)
         eo = np.abs(o_g[toks, heads].astype(np.float64) - o_ref).max()
         el = np.abs(l_g[heads, toks].astype(np.float64) - l_ref).max()
-    say(f"  {w.name}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
-    assert np.isfinite(o_g).all() and np.isfinite(l_g).all()
+        what = f"{len(toks)} sampled rows"
+    say(f"  {w.name}: {what}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
     assert eo <= O_TOL, eo
     assert el <= LSE_TOL, el
+
+
+def parity_mode(i):
+    """How much of workload i the oracle checks: everything in one call for
+    the small ones, every row in parallel units for GRPO and heterogeneous,
+    sampled rows for long-prefix (its oracle alone takes minutes)."""
+    return True if i <= 1 else ("units" if i <= 3 else False)
 
 
 # --------------------------------------------------------------- positions --
@@ -185,45 +224,54 @@ def test_attention_against_oracle(i):
     say(f"attn: workload {w.name} T={w.total_tokens} heads={w.num_q_heads}/{w.num_kv_heads}")
     L = layout_of(w)
     q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
-    o, lse = pg.pg_attn_fwd(L, q, k, v, w.softmax_scale)
+    o, lse = poisoned_outputs(q, w.num_q_heads)
+    pg.pg_attn_fwd(L, q, k, v, w.softmax_scale, o=o, lse=lse)
     torch.cuda.synchronize()
     lay = oracle_layout(w)
     check_attn(w, o, lse, host_vals(w, qkv["q"]), host_vals(w, qkv["k"]),
-               host_vals(w, qkv["v"]), lay, full=(i <= 1))
+               host_vals(w, qkv["v"]), lay, full=parity_mode(i))
 
 
-@pytest.mark.parametrize("i", [0, 1, 2, 4])
+@pytest.mark.parametrize("i", range(5))
 def test_pipeline_against_oracle(i):
     """positions -> RoPE -> attention, against the oracle pipeline (RoPE output
-    rounded to the storage dtype where the GPU hands it over)."""
+    rounded to the storage dtype where the GPU hands it over). Every row on
+    the tiny, DPO and heterogeneous workloads (the last mixes unshared and
+    shared groups on a 1024-token prompt); sampled rows on GRPO, whose every
+    row the attention-only test checks, and on long-prefix."""
     w, qkv = workload_inputs(i)
     say(f"pipeline: workload {w.name}")
     L = layout_of(w)
     pos = pg.pg_position_ids(L)
     q, k, v = (to_dev(w, qkv[n]) for n in ("q", "k", "v"))
     qr, kr = pg.pg_rope(L, pos, q, k)
-    o, lse = pg.pg_attn_fwd(L, qr, kr, v, w.softmax_scale)
+    o, lse = poisoned_outputs(q, w.num_q_heads)
+    pg.pg_attn_fwd(L, qr, kr, v, w.softmax_scale, o=o, lse=lse)
     torch.cuda.synchronize()
+    del qr, kr
     lay = oracle_layout(w)
     opos = O.positions(lay)
     qh, kh, vh = (host_vals(w, qkv[n]) for n in ("q", "k", "v"))
-    k_ref = O.storage_round(O.rope(kh, opos, w.rope_theta), w.dtype)
-    if i <= 1:
-        q_ref = O.storage_round(O.rope(qh, opos, w.rope_theta), w.dtype)
-        check_attn(w, o, lse, q_ref, k_ref, vh, lay, full=True)
-    else:
-        # roped Q only where sampled rows need it
-        toks, heads = sample_rows(lay, w.total_tokens, w.num_q_heads, 200, 99)
-        q_ref = np.zeros((w.total_tokens, w.num_q_heads, w.head_dim), dtype=np.float32)
-        q_ref[toks] = O.storage_round(O.rope(qh[toks], opos[toks], w.rope_theta), w.dtype)
-        o_ref, l_ref = O.attention_rows(q_ref, k_ref, vh, lay, w.softmax_scale, w.num_q_heads,
-                                        w.num_kv_heads, toks, heads)
-        o_g = to_host_f32(o)
-        l_g = lse.cpu().numpy()
-        eo = np.abs(o_g[toks, heads] - o_ref).max()
-        el = np.abs(l_g[heads, toks] - l_ref).max()
-        say(f"  {w.name}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
-        assert eo <= O_TOL and el <= LSE_TOL
+    k_ref = O.storage_round(O.rope(kh, opos, w.rope_theta), w.dtype).astype(np.float32)
+    if i <= 1 or i == 3:
+        # bf16-rounded values are exact in float32
+        q_ref = O.storage_round(O.rope(qh, opos, w.rope_theta), w.dtype).astype(np.float32)
+        check_attn(w, o, lse, q_ref, k_ref, vh, lay, full=(True if i <= 1 else "units"))
+        return
+    # roped Q only where sampled rows need it
+    o_g = to_host_f32(o)
+    l_g = lse.cpu().numpy()
+    assert np.isfinite(o_g).all() and np.isfinite(l_g).all()
+    toks, heads = sample_rows(lay, w.total_tokens, w.num_q_heads, 600, 99)
+    q_ref = np.zeros((w.total_tokens, w.num_q_heads, w.head_dim), dtype=np.float32)
+    ut = np.unique(toks)
+    q_ref[ut] = O.storage_round(O.rope(qh[ut], opos[ut], w.rope_theta), w.dtype)
+    o_ref, l_ref = O.attention_rows(q_ref, k_ref, vh, lay, w.softmax_scale, w.num_q_heads,
+                                    w.num_kv_heads, toks, heads)
+    eo = np.abs(o_g[toks, heads] - o_ref).max()
+    el = np.abs(l_g[heads, toks] - l_ref).max()
+    say(f"  {w.name}: {len(toks)} sampled rows: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= O_TOL and el <= LSE_TOL
 
 
 EDGE = [

@@ -43,13 +43,26 @@ def test_single_pair_equals_pair_call(w):
 
 
 def test_single_pair_argument_errors_on_device():
+    """Malformed pair arguments are refused before any launch; every pointer
+    passed is a real device tensor of the right size, so nothing here depends
+    on the order of the checks."""
     w = make_workload(0)
     L = pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
                            w.num_kv_heads, w.head_dim, w.rope_theta)
     from shared_prefix_packed_amd import _lib
     import ctypes
     lib = _lib.load()
-    d = ctypes.c_void_p(16)
-    assert lib.pg_rope(L.handle, d, None, None, None, None, 0, None) == -1   # nothing to rotate
-    assert lib.pg_rope(L.handle, d, d, None, None, None, 0, None) == -1      # half a pair
-    assert lib.pg_rope(L.handle, None, d, d, d, d, 0, None) == -1            # no positions
+    x = draw_qkv(w)
+    q, k = dev(w, x["q"]), dev(w, x["k"])
+    pos = pg.pg_position_ids(L)
+    q_out, k_out = torch.empty_like(q), torch.empty_like(k)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    torch.cuda.synchronize()
+    # nothing to rotate
+    assert lib.pg_rope(L.handle, P(pos), None, None, None, None, 0, None) == -1
+    # half a pair: an input without its output, an output without its input
+    assert lib.pg_rope(L.handle, P(pos), P(q), None, None, None, 0, None) == -1
+    assert lib.pg_rope(L.handle, P(pos), None, None, None, P(k_out), 0, None) == -1
+    # no positions
+    assert lib.pg_rope(L.handle, None, P(q), P(k), P(q_out), P(k_out), 0, None) == -1
+    torch.cuda.synchronize()

@@ -172,6 +172,22 @@ def test_attention_rows_match_full_oracle():
     assert np.abs(oo - o[:, 0]).max() <= 1e-12 and np.abs(ll - lse[0]).max() <= 1e-12
 
 
+def test_attention_rows_match_full_oracle_gqa_any_order():
+    """Rows requested in any order, with repeats and several heads per token
+    and KV head, equal the definition's rows."""
+    lay, q, k, v = _case(([7, 3], [[4, 2], [5]]), hq=6, hkv=2, d=8, seed=21)
+    o, lse = O.attention(q, k, v, lay, 0.3, 6, 2)
+    T = q.shape[0]
+    r = np.random.default_rng(4)
+    toks = np.concatenate([np.repeat(np.arange(T), 6), r.integers(0, T, size=50)])
+    heads = np.concatenate([np.tile(np.arange(6), T), r.integers(0, 6, size=50)])
+    perm = r.permutation(len(toks))
+    toks, heads = toks[perm], heads[perm]
+    oo, ll = O.attention_rows(q, k, v, lay, 0.3, 6, 2, toks, heads)
+    assert np.abs(oo - o[toks, heads]).max() <= 1e-12
+    assert np.abs(ll - lse[heads, toks]).max() <= 1e-12
+
+
 # ---------------------------------------------------------------- RoPE pins --
 
 def test_rope_position_zero_is_identity():
