@@ -167,6 +167,11 @@ pg_status pg_build_layout_host(int32_t num_groups, const int32_t* prefix_lens,
  * per-device cache of upload buffers that the library keeps until the process
  * ends. Never waits for the device. Calling it again is a no-op.
  * PG_ERR_HIP / PG_ERR_OOM on failure.
+ *
+ * Graph capture: when this call or any compute call with the layout is made
+ * on a stream under capture, the layout's upload buffer is never reused,
+ * even after pg_layout_destroy, so a captured graph stays valid for the life
+ * of the process (the buffer is held that long).
  */
 pg_status pg_layout_upload(pg_layout* layout, hipStream_t stream);
 
@@ -213,8 +218,9 @@ pg_status pg_layout_copy_decode_work(const pg_layout* layout, pg_dec_item* items
  * and is reused only after the work already enqueued with this layout has
  * completed on every stream it was used on (an event is recorded after each
  * enqueue), so no pending call is cut short. A layout used on more than four
- * distinct streams makes this call wait for its device instead. NULL is
- * ignored. */
+ * distinct streams makes this call wait for its device instead. A layout used
+ * under graph capture keeps its buffer reserved (see pg_layout_upload), so
+ * the graph may be replayed after this call. NULL is ignored. */
 void pg_layout_destroy(pg_layout* layout);
 
 /*

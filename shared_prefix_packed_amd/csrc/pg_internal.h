@@ -23,13 +23,18 @@ struct pg_slot {
   int nev = 0;
   bool overflow = false;               // used on more streams than events
   bool in_use = false;
+  bool captured = false;               // used while a stream was being captured:
+                                       // a graph may read it at any later time
 };
 // Takes an idle slot of at least `bytes` on `device` (the current device) or
 // makes one. Never waits for the device.
 pg_status pg_slot_acquire(int device, size_t bytes, pg_slot** out);
-// Records the slot's event for `stream` after work was enqueued there.
+// Records the slot's event for `stream` after work was enqueued there. On a
+// stream under graph capture an event record marks nothing on the device, so
+// the slot is marked captured instead and is never reused.
 void pg_slot_note_use(pg_slot* s, hipStream_t stream);
-// Returns the slot; it is reused once its recorded events have completed.
+// Returns the slot; it is reused once its recorded events have completed,
+// except a captured slot, which stays reserved until the process ends.
 void pg_slot_release(pg_slot* s);
 
 struct pg_layout {

@@ -8,6 +8,14 @@
 //
 // Slots are kept for the life of the process (they are small: the per-token
 // descriptors and the work list of one batch).
+//
+// Graph capture: an event recorded on a capturing stream becomes a node of
+// the graph and says nothing about when the graph's replays read the slot, and
+// a captured upload copy re-reads the pinned staging area on every replay. A
+// slot touched while a stream is capturing is therefore marked captured and
+// is never handed out again, so a graph stays valid after the layout it was
+// captured with is destroyed (the slot's memory is held until the process
+// ends).
 #include <mutex>
 #include <vector>
 
@@ -95,9 +103,24 @@ pg_status pg_slot_acquire(int device, size_t bytes, pg_slot** out) {
   return PG_OK;
 }
 
+// True unless `stream` is known not to be capturing (an error counts as
+// capturing: the slot is then kept, which is always safe).
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
 void pg_slot_note_use(pg_slot* s, hipStream_t stream) {
   if (!s) return;
   std::lock_guard<std::mutex> lock(s->mu);
+  if (stream_capturing(stream)) {
+    s->captured = true;
+    return;
+  }
   int i = 0;
   while (i < s->nev && s->stream[i] != stream) ++i;
   if (i == kSlotEvents) {
@@ -121,6 +144,10 @@ void pg_slot_note_use(pg_slot* s, hipStream_t stream) {
 
 void pg_slot_release(pg_slot* s) {
   if (!s) return;
+  {
+    std::lock_guard<std::mutex> lock(s->mu);
+    if (s->captured) return;   // a captured graph may still read it: never reused
+  }
   if (s->overflow) {
     int cur = -1;
     (void)hipGetDevice(&cur);

@@ -94,3 +94,51 @@ def test_hot_path_replays_bit_exactly_under_graph_capture():
         print(f"  replay {rep}: all {len(outs)} outputs bit-identical to the eager run", flush=True)
     del g
     L.close()
+
+
+def test_graph_replays_after_its_layout_is_destroyed():
+    """A layout used under capture keeps its upload buffer: after the layout
+    is destroyed and new layouts of the same size are built, uploaded and used
+    (which recycles every idle buffer), the graph still replays the captured
+    forward bit for bit."""
+    w = make_workload(1)
+    L = pg.pg_build_layout(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
+                           w.num_kv_heads, w.head_dim, w.rope_theta)
+    q, k, v = (dev(draw_tensor(w, n)) for n in ("q", "k", "v"))
+    T, Hq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pg.pg_attn_fwd(L, q, k, v, w.softmax_scale, o=o, lse=lse, stream=side)
+    torch.cuda.synchronize()
+    ref = (o.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pg.pg_attn_fwd(L, q, k, v, w.softmax_scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    L.close()
+    # other layouts of the same size (other lengths, so other tables) take
+    # every idle upload buffer and overwrite it
+    others = []
+    for seed in range(4):
+        pl = np.roll(w.prefix_lens, seed + 1)
+        sl = np.roll(w.suffix_lens, 2 * seed + 1)
+        L2 = pg.pg_build_layout(pl, w.suffix_counts, sl, w.num_q_heads, w.num_kv_heads,
+                                w.head_dim, w.rope_theta)
+        pg.pg_position_ids(L2)
+        others.append(L2)
+    torch.cuda.synchronize()
+    for L2 in others:
+        L2.close()
+    for rep in range(2):
+        o.view(torch.uint8).fill_(0xFF)
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16)), rep
+        assert torch.equal(lse, ref[1]), rep
+    print("  graph replayed bit-identically after its layout was destroyed", flush=True)
+    del g
