@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import argparse
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,6 +46,46 @@ def _run(cmd, verbose):
     return out
 
 
+M0_WRITE = re.compile(r"^\s*s_mov_b32\s+m0,\s*s\d+\b")
+LDS_LOAD = re.compile(r"^\s*buffer_load_dword(x4)?\s.*\blds\b")
+
+
+def check_m0(obj: str, verbose: bool = False) -> int:
+    """Scan the gfx950 disassembly of a HIP object built here for M0.
+
+    The buffer -> LDS loads are inline asm that set M0 (the LDS destination)
+    one wait state before the load; the compiler cannot be told that M0 is
+    clobbered. That is safe only while no compiler-generated code uses M0,
+    so every instruction of the object that mentions M0 must be one of those
+    writes, immediately followed by s_nop 0 and the load that reads it.
+    Raises if anything else touches M0. Returns the number of sequences."""
+    llvm = os.path.join(ROCM, "llvm", "bin")
+    tmp = obj + ".m0check"
+    try:
+        _run([os.path.join(llvm, "llvm-objcopy"), f"--dump-section=.hip_fatbin={tmp}.fb", obj], verbose)
+        _run([os.path.join(llvm, "clang-offload-bundler"), "--type=o", f"--input={tmp}.fb",
+              f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}", f"--output={tmp}.co", "--unbundle"],
+             verbose)
+        dis = _run([os.path.join(llvm, "llvm-objdump"), "-d", f"--mcpu={ARCH}", f"{tmp}.co"], False)
+    finally:
+        for ext in (".fb", ".co"):
+            if os.path.exists(tmp + ext):
+                os.remove(tmp + ext)
+    lines = [l.split("//")[0].rstrip() for l in dis.splitlines()]
+    lines = [l for l in lines if l.strip() and l.startswith(("\t", " "))]
+    n = 0
+    for i, l in enumerate(lines):
+        if not re.search(r"\bm0\b", l):
+            continue
+        ok = (M0_WRITE.match(l) and i + 2 < len(lines) and lines[i + 1].split() == ["s_nop", "0"]
+              and LDS_LOAD.match(lines[i + 2]))
+        if not ok:
+            raise RuntimeError(f"{os.path.basename(obj)}: M0 used outside the buffer->LDS load "
+                               f"sequences: {l.strip()!r}")
+        n += 1
+    return n
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     cxx = shutil.which("g++") or "g++"
@@ -61,6 +102,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
         reports.append(_run([hipcc, *HIP_FLAGS, *extra, *incs, "-c", os.path.join(CSRC, src),
                              "-o", obj], verbose))
+        check_m0(obj, verbose)
         objs.append(obj)
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)

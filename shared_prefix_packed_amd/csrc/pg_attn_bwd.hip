@@ -59,8 +59,9 @@ __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // 4 bytes per lane from buffer `r` at byte offset `voff` into LDS at
-// lds + 4 * lane (M0 written one wait state before the load, as for the
-// 16-byte form).
+// lds + 4 * lane. Same invariant as buf16_to_lds: M0 is written one wait
+// state before the load that reads it, and the build's M0 check fails if any
+// other instruction of the object touches M0.
 __device__ inline void buf4_to_lds(i32x4_t r, int voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"

@@ -38,12 +38,18 @@ __device__ inline i32x4_t make_rsrc(const void* base, int bytes) {
 
 // 16 bytes per lane from buffer `r` at byte offset `voff` straight into LDS at
 // byte address lds + 16 * lane (lds is wave-uniform). Written as asm so the
-// compiler does not guard every later LDS read with a full vmcnt(0) wait: the
-// loads only write LDS (no VGPR result), and their completion is awaited
-// explicitly (wait_vmem_*) before the barrier that publishes the tile. M0 is
-// written here, one wait state before the load that reads it; the compiler
-// keeps no value in M0 across these kernels' code (no M0-relative LDS
-// instruction is used, checked in the generated code).
+// compiler does not guard later LDS reads with full vmcnt(0) waits: the loads
+// only write LDS (no VGPR result), and their completion is awaited explicitly
+// (wait_vmem_*) before the barrier that publishes the tile. With the builtin
+// __builtin_amdgcn_raw_ptr_buffer_load_lds the compiler owns M0 but cannot
+// tell the ring stages apart, and waits for every load in flight before LDS
+// reads (six more vmcnt(0) waits in the forward's tile loop), which drains
+// the tiles fetched ahead.
+// Invariant: M0 is written here, one wait state before the load that reads
+// it, and the compiler cannot be told so (M0 is not accepted in a clobber
+// list). This is safe only while no compiler-generated code in these kernels
+// uses M0; the build (build.py, check_m0) disassembles every HIP object and
+// fails if any instruction other than these sequences touches M0.
 __device__ inline void buf16_to_lds(i32x4_t r, int voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
