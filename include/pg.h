@@ -372,6 +372,32 @@ pg_status pg_attn_decode(const pg_layout* layout, const void* q, const void* k_c
                          void* workspace, size_t workspace_bytes, pg_dtype dtype,
                          float softmax_scale, hipStream_t stream);
 
+/* Size of the static device array pg_attn_decode_noalloc keeps its partial
+ * results in (one copy per GPU, held until the process ends): 32 MiB, which
+ * covers a decode step of up to 2016 work items at d = 128. */
+#define PG_DECODE_SCRATCH_BYTES (32u << 20)
+
+/*
+ * pg_attn_decode_noalloc -- pg_attn_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * results and errors as pg_attn_decode, bit-identical outputs (same kernels);
+ * the bf16, d = 128 kernel keeps its partial results in a library-owned
+ * static device array of PG_DECODE_SCRATCH_BYTES on the current GPU instead.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library call. The
+ * array's device address is looked up on the first call on each GPU.
+ * PG_ERR_INVALID_ARG (before any launch) when the layout's step needs more
+ * than PG_DECODE_SCRATCH_BYTES (pg_decode_workspace_size tells); nothing in
+ * the array needs to start at zero (every partial a step reads is written by
+ * that step first). Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents: calls that overlap on one GPU (other streams,
+ * other threads, without ordering between them) race, and the caller must
+ * order them.
+ */
+pg_status pg_attn_decode_noalloc(const pg_layout* layout, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* cur_lens, void* o, float* lse,
+                                 pg_dtype dtype, float softmax_scale, hipStream_t stream);
+
 /*
  * Right-padded compatibility form. The verl page (sections 1-2) keeps a batch
  * as [G, max_len]: row g is group g's packed row (prompt, then each response),

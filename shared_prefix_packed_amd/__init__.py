@@ -8,6 +8,7 @@ from .api import (  # noqa: F401
     Layout,
     pg_attn_bwd,
     pg_attn_decode,
+    pg_attn_decode_noalloc,
     pg_attn_fwd,
     pg_build_layout,
     pg_build_layout_host,

@@ -11,6 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpg.so")
 
 PG_OK = 0
+PG_DECODE_SCRATCH_BYTES = 32 << 20   # include/pg.h
 PG_F32 = 0
 PG_BF16 = 1
 
@@ -80,6 +81,8 @@ SIGNATURES = {
     "pg_attn_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, ctypes.c_size_t, c_int32, ctypes.c_float,
                                  c_void_p]),
+    "pg_attn_decode_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_int32, ctypes.c_float, c_void_p]),
     "pg_layout_destroy": (None, [c_void_p]),
     "pg_position_ids": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "pg_rope": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,

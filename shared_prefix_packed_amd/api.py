@@ -318,6 +318,32 @@ def pg_attn_decode(layout: Layout, q, k_cache, v_cache, cur_lens, softmax_scale:
     return o, lse
 
 
+def pg_attn_decode_noalloc(layout: Layout, q, k_cache, v_cache, cur_lens, softmax_scale: float,
+                           o=None, lse=None, stream=None):
+    """pg_attn_decode without a workspace: the library keeps the partial
+    results in its static per-GPU scratch array. The C call allocates
+    nothing; pass o and lse to allocate nothing here either."""
+    import torch
+    T, Hq, Hkv, d = layout.total_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    N = layout.num_responses
+    _check_tensor("q", q, (N, Hq, d))
+    _check_tensor("k_cache", k_cache, (T, Hkv, d), q.dtype)
+    _check_tensor("v_cache", v_cache, (T, Hkv, d), q.dtype)
+    _check_tensor("cur_lens", cur_lens, (N,), torch.int32)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, (N, Hq, d), q.dtype)
+    _check_tensor("lse", lse, (Hq, N), torch.float32)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    check(load().pg_attn_decode_noalloc(layout.handle, ptr(q), ptr(k_cache), ptr(v_cache),
+                                        ptr(cur_lens), ptr(o), ptr(lse), _dtype_code(q),
+                                        float(softmax_scale), _stream_handle(stream)),
+          "pg_attn_decode_noalloc")
+    return o, lse
+
+
 def _row_bytes(t, lead: int) -> int:
     n = 1
     for x in t.shape[lead:]:

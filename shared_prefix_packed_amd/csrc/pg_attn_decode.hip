@@ -25,6 +25,8 @@
 //    partials of the items holding its row (O = sum e^(m_i - M) O_i / sum
 //    e^(m_i - M) l_i) and writes O (bf16) and lse; the partials are fetched
 //    side by side, one lane each, rather than one after another.
+#include <mutex>
+
 #include "pg_hip_common.h"
 #include "pg_internal.h"
 
@@ -320,4 +322,36 @@ hipError_t pg_launch_attn_decode(const pg_layout& L, const void* q, const void* 
       ws_o, ws_ml, tables ? L.d_dec_items : nullptr, tables ? L.d_dec_ref_off : nullptr,
       tables ? L.d_dec_refs : nullptr, static_cast<uint16_t*>(o), lse, N, L.Hq, L.Hkv, r);
   return hipGetLastError();
+}
+
+// ------------------------------------------------- decode without a workspace --
+//
+// For callers that cannot allocate device memory, the partial results can live
+// in a static device array instead of a caller workspace. Each GPU the library
+// runs on holds its own copy until the process ends. In host code the array's
+// name is only a stand-in for the device copy: its device address is looked up
+// once per device with hipGetSymbolAddress (the device current) and only that
+// address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PG_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t pg_decode_scratch(int device, void** ptr) {
+  *ptr = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
 }

@@ -331,6 +331,36 @@ pg_status pg_decode_workspace_size(const pg_layout* L, size_t* bytes) {
   return PG_OK;
 }
 
+pg_status pg_attn_decode_noalloc(const pg_layout* L, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* cur_lens, void* o, float* lse,
+                                 pg_dtype dtype, float softmax_scale, hipStream_t stream) {
+  pg_status s = check_device_layout(L);
+  if (s != PG_OK) return s;
+  if (dtype != PG_BF16 && dtype != PG_F32) return pg_fail(PG_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return pg_fail(PG_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  const int64_t N = int64_t(L->suffix_lens.size());
+  if (N == 0) return PG_OK;
+  if (!q || !o || !lse || !cur_lens) return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (L->T > 0 && (!k_cache || !v_cache)) return pg_fail(PG_ERR_INVALID_ARG, "NULL cache pointer");
+  if (N * L->Hq > int64_t(0x7fffffff)) return pg_fail(PG_ERR_INVALID_ARG, "too many query rows");
+  void* scratch = nullptr;
+  if (dtype == PG_BF16 && L->d == 128) {
+    const size_t need = pg_decode_workspace_bytes(*L);
+    if (need > size_t(PG_DECODE_SCRATCH_BYTES))
+      return pg_fail(PG_ERR_INVALID_ARG,
+                     "decode step needs %zu bytes of scratch, more than the %zu of the static "
+                     "array (use pg_attn_decode with a workspace)",
+                     need, size_t(PG_DECODE_SCRATCH_BYTES));
+    hipError_t e = pg_decode_scratch(L->device, &scratch);
+    if (e != hipSuccess) return hip_fail(e, "decode scratch address");
+  }
+  hipError_t e = pg_launch_attn_decode(*L, q, k_cache, v_cache, cur_lens, o, lse, scratch, dtype,
+                                       softmax_scale, stream);
+  pg_slot_note_use(L->slot, stream);
+  return e == hipSuccess ? PG_OK : hip_fail(e, "decode kernel launch");
+}
+
 pg_status pg_attn_decode(const pg_layout* L, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* cur_lens, void* o, float* lse,
                          void* workspace, size_t workspace_bytes, pg_dtype dtype,

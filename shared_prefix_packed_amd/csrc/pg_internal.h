@@ -132,6 +132,9 @@ hipError_t pg_launch_decode_rowwise(const pg_layout& L, const void* q, const voi
                                    pg_dtype dtype, float softmax_scale, hipStream_t stream);
 // Workspace bytes of the decode kernel for layout L (one partial per item).
 size_t pg_decode_workspace_bytes(const pg_layout& L);
+// Device address of the static decode scratch array (PG_DECODE_SCRATCH_BYTES)
+// on `device`, which must be the current device; looked up once per device.
+hipError_t pg_decode_scratch(int device, void** ptr);
 hipError_t pg_launch_attn_bwd(const pg_layout& L, const void* q, const void* k, const void* v,
                               const void* o, const float* lse, const void* dout, void* dq,
                               void* dk, void* dv, float* delta, float softmax_scale,
