@@ -8,7 +8,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpg.so")
+# PG_LIBRARY may name another build of the same library (the sanitizer build
+# of the host code, python -m shared_prefix_packed_amd.build --sanitize).
+LIB_PATH = os.environ.get("PG_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpg.so")
 
 PG_OK = 0
 PG_DECODE_SCRATCH_BYTES = 32 << 20   # include/pg.h

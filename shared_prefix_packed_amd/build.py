@@ -1,9 +1,19 @@
 """Build libpg.so in-tree: host C++ with g++, HIP kernels with hipcc for gfx950.
 
-    python -m shared_prefix_packed_amd.build [--resource-usage]
+    python -m shared_prefix_packed_amd.build [--resource-usage] [--sanitize]
 
 Objects go to ``_build/`` at the repository root; the library lands next to
 this file as ``libpg.so``. Every call recompiles.
+
+``--sanitize`` builds a second copy, ``_build/sanitize/libpg.so``, whose host
+C++ (layout builder, C ABI, upload-slot cache) is compiled by g++ with
+AddressSanitizer and UndefinedBehaviorSanitizer (aborting on the first
+report); its HIP kernels are the ordinary ones. Load it with PG_LIBRARY and
+preload gcc's sanitizer runtimes, e.g.
+
+    PG_LIBRARY=_build/sanitize/libpg.so \
+    LD_PRELOAD="$(gcc -print-file-name=libasan.so) $(gcc -print-file-name=libubsan.so)" \
+    ASAN_OPTIONS=detect_leaks=0 python -m pytest tests/test_host_layout.py tests/test_host_threads.py
 """
 from __future__ import annotations
 
@@ -86,6 +96,32 @@ def check_m0(obj: str, verbose: bool = False) -> int:
     return n
 
 
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Host C++ with ASan + UBSan (g++), HIP kernels as usual; returns the
+    path of the sanitizer build of the library."""
+    build(verbose)   # the HIP objects and the M0 check
+    cxx = shutil.which("g++") or "g++"
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    incs = [f"-I{INCLUDE}", f"-I{CSRC}", f"-I{os.path.join(ROCM, 'include')}"]
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(SANITIZE_DIR, src + ".o")
+        _run([cxx, *HOST_FLAGS, *SANITIZE_FLAGS, *incs, "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
+        objs.append(obj)
+    objs += [os.path.join(BUILD_DIR, src + ".o") for src in HIP_SOURCES]
+    out = os.path.join(SANITIZE_DIR, "libpg.so")
+    # the sanitizer runtimes come from LD_PRELOAD at run time
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out], verbose)
+    return out
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     cxx = shutil.which("g++") or "g++"
@@ -116,10 +152,14 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--resource-usage", action="store_true",
                     help="print per-kernel VGPR/AGPR/LDS/occupancy from the compiler")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="also build _build/sanitize/libpg.so: host C++ under ASan + UBSan")
     ap.add_argument("-v", "--verbose", action="store_true")
     args = ap.parse_args(argv)
     path = build(verbose=args.verbose, resource_usage=args.resource_usage)
     print(path)
+    if args.sanitize:
+        print(build_sanitized(verbose=args.verbose))
 
 
 if __name__ == "__main__":
