@@ -80,10 +80,12 @@ typedef struct pg_layout_summary {
 
 /* One work item of the attention launch: query tokens [t0, t1) of one group,
  * query heads [hq0, hq0 + heads_per_item), keys from spans
- * [span0, span0 + nspan) of the span list. Items are stored in launch order:
- * item p runs on XCD p % 8; every item of one (group, KV head) sits on one
- * XCD, and each XCD's items are in cost-descending order per cluster. Items
- * with nspan == 0 are padding and do nothing. */
+ * [span0, span0 + nspan) of the span list, walked in ntiles tiles of 64 keys;
+ * k0 and k1 repeat the first span, so a kernel can fetch its first tiles
+ * without reading the span list. Items are stored in launch order: item p
+ * runs on XCD p % 8; every item of one (group, KV head) sits on one XCD, and
+ * each XCD's items are in cost-descending order per cluster. Items with
+ * nspan == 0 are padding and do nothing. */
 typedef struct pg_work_item {
   int32_t t0;
   int32_t t1;
@@ -91,6 +93,10 @@ typedef struct pg_work_item {
   int32_t pe;     /* end of the group's prefix (absolute token index)       */
   int32_t span0;
   int32_t nspan;
+  int32_t ntiles; /* sum over the spans of ceil(span length / 64)            */
+  int32_t k0;     /* the first span, spans[span0]                            */
+  int32_t k1;
+  int32_t reserved;
   int64_t cost;   /* allowed (query, key) pairs of the item x its heads      */
 } pg_work_item;
 

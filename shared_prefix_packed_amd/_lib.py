@@ -49,7 +49,8 @@ class LayoutSummary(ctypes.Structure):
 
 class WorkItem(ctypes.Structure):
     _fields_ = [("t0", c_int32), ("t1", c_int32), ("hq0", c_int32), ("pe", c_int32),
-                ("span0", c_int32), ("nspan", c_int32), ("cost", c_int64)]
+                ("span0", c_int32), ("nspan", c_int32), ("ntiles", c_int32),
+                ("k0", c_int32), ("k1", c_int32), ("reserved", c_int32), ("cost", c_int64)]
 
 
 class KeySpan(ctypes.Structure):

@@ -89,7 +89,9 @@ class Layout:
         check(load().pg_layout_copy_work(self.handle, items, spans), "pg_layout_copy_work")
         it = np.frombuffer(items, dtype=np.dtype([("t0", "<i4"), ("t1", "<i4"), ("hq0", "<i4"),
                                                   ("pe", "<i4"), ("span0", "<i4"),
-                                                  ("nspan", "<i4"), ("cost", "<i8")]))
+                                                  ("nspan", "<i4"), ("ntiles", "<i4"),
+                                                  ("k0", "<i4"), ("k1", "<i4"),
+                                                  ("reserved", "<i4"), ("cost", "<i8")]))
         sp = np.frombuffer(spans, dtype=np.int32).reshape(-1, 2)
         return it[:s.num_items].copy(), sp[:s.num_spans].copy()
 

@@ -99,6 +99,11 @@ __device__ inline void step_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The fields of a work item the kernel uses (read with scalar loads).
+struct Item {
+  int t0, t1, hq0, pe, span0, nspan, ntiles, k0, k1;
+};
+
 // Walks the 64-key tiles of an item's key spans (all scalar state).
 struct TileIter {
   int s, s_end, ka;
@@ -133,7 +138,26 @@ struct TileIter {
 __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
 
-  const pg_work_item it = a.items[blockIdx.x];
+  // the whole item in one scalar load, before the padding test
+  Item it;
+  {
+    const __attribute__((address_space(4))) int* c =
+        (const __attribute__((address_space(4))) int*)(a.items + blockIdx.x);
+    it.t0 = c[0];
+    it.t1 = c[1];
+    it.hq0 = c[2];
+    it.pe = c[3];
+    it.span0 = c[4];
+    it.nspan = c[5];
+    it.ntiles = c[6];
+    it.k0 = c[7];
+    it.k1 = c[8];
+  }
+  // every field in hand before the padding test, so that the item costs one
+  // scalar load round trip, not one for the test and another after it
+  asm volatile("" ::"s"(it.t0), "s"(it.t1), "s"(it.hq0), "s"(it.pe), "s"(it.span0),
+               "s"(it.nspan), "s"(it.ntiles), "s"(it.k0), "s"(it.k1), "s"(a.Hkv), "s"(a.hpw),
+               "s"(a.r));
   if (it.nspan == 0) return;   // padding of a shorter XCD queue
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,6 +166,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   const int wg = wave & 3;      // wave inside its group
   const int qi = lane & 31;     // query column of this lane inside the wave
   const int half = lane >> 5;   // which half of each 16-wide k step the lane feeds
+  const int ntiles = __builtin_amdgcn_readfirstlane(it.ntiles);
 
   const int h = it.hq0 + wave % a.hpw;
   const int hk = it.hq0 / a.r;   // one KV head per item
@@ -151,40 +176,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   const int tq = wave_active ? min(tb + qi, te - 1) : it.t0;   // padded rows repeat the last one
   const bool row_valid = wave_active && (tb + qi < te);
 
-  // Masked keys get p = 0, which multiplies V: V slots must never hold a NaN
-  // pattern, so the V half of every stage starts out zero.
-  for (int i = tid; i < NSTAGE * V_BYTES / 16; i += 64 * NWAVES) {
-    const int st = i / (V_BYTES / 16), o = i % (V_BYTES / 16);
-    *reinterpret_cast<uint4*>(smem + st * STAGE + K_BYTES + 16 * o) = make_uint4(0, 0, 0, 0);
-  }
-
-  // Q as the B operand of S^T = K Q^T: lane holds d = 16 ks + 8 half + 0..7.
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qrow = a.q + (int64_t(tq) * a.Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 16 * ks));
-  }
-  const int ss_t = a.tok_ss[tq];
-  int ss_max = ss_t;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss_max = max(ss_max, __shfl_xor(ss_max, off, 64));
-
-  f32x16_t acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  float m_run = -1.0e30f;   // finite start: exp2(m_run - m_new) is 0, never NaN
-  float l_run = 0.f;
-
-  // number of tiles of this item
-  int ntiles = 0;
-  for (int s = it.span0; s < it.span0 + it.nspan; ++s) {
-    const pg_key_span sp = a.spans[s];
-    ntiles += (sp.k1 - sp.k0 + KT - 1) / KT;
-  }
-
   // ---- staging: per-lane global byte offsets from a tile's first key row ----
   // Wave wg of a group writes LDS blocks 4 wg + i (i = 0..3) of 1 KB each.
   // K block b = rows 4b..4b+3: lane L -> row 4b + L/16, stored chunk L%16,
@@ -192,6 +183,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   // V block b = 512-byte read blocks 2b, 2b+1 (block index ks*8 + rd*4 + db);
   //   16-byte unit u of a read block holds V[16ks + 8rd + 4(u/16) + (u%8)/2]
   //   [32db + 16((u/8)&1) + 8(u&1) .. +8].
+  // Rows past a span's end read as zero (the buffer descriptor ends at the
+  // span), so every stage a product reads holds finite values only.
   const int row_bytes = a.Hkv * D * 2;
   int goff[LOADS_PER_TILE];
 #pragma unroll
@@ -227,6 +220,44 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
     for (int i = 0; i < LOADS_PER_TILE; ++i) buf16_to_lds(rs, goff[i], dst + 1024 * i);
   };
 
+  // Prologue. Its memory latencies are the cost of every work item that no
+  // other work hides (one workgroup per compute unit), so the first two tile
+  // fetches go out first, from the item's own copy of its first span (no span
+  // list read before them), and Q and the segment starts are loaded while
+  // they are in flight; a single wait covers all of them.
+  TileIter ld;
+  ld.s = __builtin_amdgcn_readfirstlane(it.span0);
+  ld.s_end = __builtin_amdgcn_readfirstlane(it.span0 + it.nspan);
+  ld.sp.k0 = __builtin_amdgcn_readfirstlane(it.k0);
+  ld.sp.k1 = __builtin_amdgcn_readfirstlane(it.k1);
+  ld.ka = ld.sp.k0;
+  gload(ld.ka, ld.sp.k1, 0);
+  ld.next(a.spans);
+  if (ntiles > 1) {
+    gload(ld.ka, ld.sp.k1, 1);
+    ld.next(a.spans);
+  }
+
+  // Q as the B operand of S^T = K Q^T: lane holds d = 16 ks + 8 half + 0..7.
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qrow = a.q + (int64_t(tq) * a.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 16 * ks));
+  }
+  const int ss_t = a.tok_ss[tq];
+  // Segment starts never decrease along a group's row, so the largest among
+  // this wave's rows is the last row's: one scalar load, no cross-lane step.
+  const int ss_max = ld_scalar(a.tok_ss, wave_active ? te - 1 : it.t0);
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float m_run = -1.0e30f;   // finite start: exp2(m_run - m_new) is 0, never NaN
+  float l_run = 0.f;
+
   // ---- LDS read offsets --------------------------------------------------
   // S: A operand of block kb, k step ks = K row 32 kb + qi, chunk 2 ks + half,
   //    stored at chunk (2 ks + half) ^ (qi & 15).
@@ -236,15 +267,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
   // PV: lane reads 8 bytes at 8 * lane of each 512-byte block.
   const int voff = K_BYTES + 8 * lane;
 
-  // Prologue: tiles 0 and 1 (K by group A, V by group B) into stages 0 and 1.
-  TileIter ld;
-  ld.init(a.spans, it.span0, it.nspan);
-  gload(ld.ka, ld.sp.k1, 0);
-  ld.next(a.spans);
-  if (ntiles > 1) {
-    gload(ld.ka, ld.sp.k1, 1);
-    ld.next(a.spans);
-  }
   // The scalar set-up of each fetch (tile bounds, buffer descriptor, LDS
   // destination) is done one step early, in the VALU step, whose scalar unit
   // is idle; the MFMA step then only issues the loads.

@@ -226,6 +226,9 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
           if (b > a && b > t0) L.spans.push_back({a, std::min(b, t1)});
         }
         const int32_t nspan = int32_t(L.spans.size()) - span0;
+        int32_t ntiles = 0;
+        for (int32_t s = span0; s < span0 + nspan; ++s)
+          ntiles += (L.spans[size_t(s)].k1 - L.spans[size_t(s)].k0 + PG_KEY_TILE - 1) / PG_KEY_TILE;
         int64_t pairs = 0;
         for (int32_t t = t0; t < t1; ++t) pairs += keys_of(t, L.tok_g0[t], L.tok_pe[t], L.tok_ss[t]);
         for (int32_t hk = 0; hk < num_kv_heads; ++hk) {
@@ -237,6 +240,10 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
             it.pe = pe;
             it.span0 = span0;
             it.nspan = nspan;
+            it.ntiles = ntiles;
+            it.k0 = nspan > 0 ? L.spans[size_t(span0)].k0 : 0;
+            it.k1 = nspan > 0 ? L.spans[size_t(span0)].k1 : 0;
+            it.reserved = 0;
             it.cost = pairs * hpw;
             L.max_item_cost = std::max(L.max_item_cost, it.cost);
             L.items.push_back(it);
@@ -269,6 +276,7 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
     for (int32_t i : pos) launch.push_back(i >= 0 ? L.items[size_t(i)] : empty);
     L.items.swap(launch);
     L.xcd_load = xcd_load;
+
 
     // Backward work list (dK, dV): blocks of PG_KV_BLOCK keys of one KV head
     // that never cross a segment. The queries that read key j form one

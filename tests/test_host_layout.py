@@ -101,7 +101,7 @@ def _check_work_invariants(L, P, S, hq, hkv):
     seen_done = set()
     for p, it in enumerate(items):
         if it["nspan"] == 0:
-            assert it["cost"] == 0 and it["t1"] == it["t0"]
+            assert it["cost"] == 0 and it["t1"] == it["t0"] and it["ntiles"] == 0
             continue
         t0, t1, hq0 = int(it["t0"]), int(it["t1"]), int(it["hq0"])
         assert 0 < t1 - t0 <= s.block_tokens
@@ -112,6 +112,9 @@ def _check_work_invariants(L, P, S, hq, hkv):
         # spans: disjoint, ascending, inside the group; their union equals the
         # union of the allowed keys of the item's tokens
         sp = spans[it["span0"]:it["span0"] + it["nspan"]]
+        # the tile count and the copy of the first span the kernel starts from
+        assert it["ntiles"] == sum((k1 - k0 + 63) // 64 for k0, k1 in sp)
+        assert (it["k0"], it["k1"]) == tuple(sp[0])
         keys = set()
         prev = -1
         for k0, k1 in sp:
