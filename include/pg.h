@@ -330,8 +330,12 @@ pg_status pg_unpack_rows(const pg_layout* layout, const void* packed, int64_t ro
  *              dk/dv is written, zero where no query reads the key)
  *  delta       caller-owned device scratch of Hq * T floats; on return it holds
  *              D = rowsum(dO * O) of every (head, token) row, fp32 [Hq, T]
- * All tensors share dtype; PG_ERR_UNSUPPORTED unless dtype == PG_BF16 and
- * d == 128. dq, dk, dv must not alias the inputs or each other.
+ * All tensors share dtype. bf16 with d = 128 runs the MFMA kernels (P and dS
+ * enter the matrix cores rounded to bf16); fp32, and bf16 with d = 64, run a
+ * reference-grade per-row path (one wave per query row, then one per key row,
+ * fp32 arithmetic throughout; for correctness checks and small problems: it
+ * reads every query row once per key that the row reads). dq, dk, dv must
+ * not alias the inputs or each other. PG_ERR_UNSUPPORTED for another dtype.
  */
 pg_status pg_attn_bwd(const pg_layout* layout, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, void* dq, void* dk,

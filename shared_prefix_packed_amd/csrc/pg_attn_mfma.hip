@@ -382,27 +382,30 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_d128(MfmaArgs a) {
         // allowed keys of this lane's query inside the span: [lo, hi] with
         // lo = own segment start (suffix spans) and hi = min(t, k1 - 1); in
         // tile-local offsets c = 32 kb + 8 (i/4) + i%4 after removing 4 half.
+        // The lane's allowed offsets become one 64-bit mask, and each score
+        // takes its bit by a signed bitfield extract (0 or -1) and a bitwise
+        // select: no compare into VCC per score (each would need wait states
+        // before its select). A 32-key block that no lane masks is skipped
+        // whole (the diagonal usually cuts only one of the two).
         const int base = v_ka + 4 * half;
         const int lo = (v_prefix ? v_ka : ss_t) - base;
         const int hi = min(tq, v_k1 - 1) - base;
-        if (__ballot(lo > 0) == 0ull) {
-          // no lane has a lower bound inside the tile (diagonal and span-end
-          // tiles): one compare per score
+        // bit c of M: tile-local key offset c in [lo, hi]
+        const int l0 = max(lo, 0), h0 = min(hi, 63);
+        const uint64_t full = ~uint64_t(0);
+        const uint64_t M = h0 < l0 ? uint64_t(0) : ((full >> (63 - h0)) & (full << l0));
 #pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-              sacc[kb2][i] = (c <= hi) ? sacc[kb2][i] : -__builtin_inff();
-            }
-        } else {
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const uint32_t w = uint32_t(M >> (32 * kb2));
+          if (__ballot((w & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) != 0ull) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-              sacc[kb2][i] = (c >= lo && c <= hi) ? sacc[kb2][i] : -__builtin_inff();
+              const int c = 8 * (i >> 2) + (i & 3);
+              const int keep = __builtin_amdgcn_sbfe(int(w), c, 1);   // -1 kept, 0 masked
+              sacc[kb2][i] = __int_as_float((__float_as_int(sacc[kb2][i]) & keep) |
+                                            (int(0xff800000u) & ~keep));
             }
+          }
         }
       }
       float mt = sacc[0][0];

@@ -309,9 +309,8 @@ pg_status pg_attn_bwd(const pg_layout* L, const void* q, const void* k, const vo
                       hipStream_t stream) {
   pg_status s = check_device_layout(L);
   if (s != PG_OK) return s;
-  if (dtype != PG_BF16 || L->d != 128)
-    return pg_fail(PG_ERR_UNSUPPORTED, "backward needs bf16 and head_dim 128 (dtype %d, d %d)",
-                   int(dtype), L->d);
+  if (dtype != PG_F32 && dtype != PG_BF16)
+    return pg_fail(PG_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return pg_fail(PG_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (L->T == 0) return PG_OK;
@@ -319,8 +318,14 @@ pg_status pg_attn_bwd(const pg_layout* L, const void* q, const void* k, const vo
     return pg_fail(PG_ERR_INVALID_ARG, "NULL tensor pointer");
   if (dq == dk || dq == dv || dk == dv)
     return pg_fail(PG_ERR_INVALID_ARG, "dq, dk, dv must be distinct buffers");
-  hipError_t e = pg_launch_attn_bwd(*L, q, k, v, o, lse, dout, dq, dk, dv, delta, softmax_scale,
-                                    stream);
+  if (L->T * L->Hq > int64_t(0x7fffffff))
+    return pg_fail(PG_ERR_INVALID_ARG, "too many query rows");
+  hipError_t e;
+  if (dtype == PG_BF16 && L->d == 128)
+    e = pg_launch_attn_bwd(*L, q, k, v, o, lse, dout, dq, dk, dv, delta, softmax_scale, stream);
+  else
+    e = pg_launch_bwd_rowwise(*L, q, k, v, o, lse, dout, dq, dk, dv, delta, dtype, softmax_scale,
+                              stream);
   pg_slot_note_use(L->slot, stream);
   return e == hipSuccess ? PG_OK : hip_fail(e, "backward kernel launch");
 }

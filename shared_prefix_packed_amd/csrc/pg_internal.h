@@ -139,6 +139,11 @@ hipError_t pg_launch_attn_bwd(const pg_layout& L, const void* q, const void* k, 
                               const void* o, const float* lse, const void* dout, void* dq,
                               void* dk, void* dv, float* delta, float softmax_scale,
                               hipStream_t stream);
+// Backward, one wave per query row then one per key row (fp32, or d = 64).
+hipError_t pg_launch_bwd_rowwise(const pg_layout& L, const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, float* delta, pg_dtype dtype,
+                                 float softmax_scale, hipStream_t stream);
 hipError_t pg_launch_attn_mfma(const pg_layout& L, const void* q, const void* k, const void* v,
                                void* o, float* lse, float softmax_scale, hipStream_t stream);
 

@@ -209,6 +209,129 @@ __global__ __launch_bounds__(64) void attn_rowwise_kernel(
 }
 
 
+// ------------------------------------------------- per-row backward --
+// The backward of the per-row forward, for fp32 and for d = 64 (the MFMA
+// kernels take bf16 with d = 128): the chain rule as the MFMA path computes
+// it, in fp32 from the stored inputs, one wave per row and no matrix units.
+// With P the softmax of query row t over K(t) (p_j = exp(scale q.k_j - lse_t),
+// from the forward's lse) and D_t = dO_t . O_t (the forward's O as stored):
+//   dQ_t = scale sum_j p_j (dO_t . v_j - D_t) k_j            (query rows)
+//   dV_j = sum p_tj dO_t,  dK_j = scale sum p_tj (dO_t . v_j - D_t) q_t
+// over the query rows t that read key j and the query heads of its KV head
+// (key rows). The rows that read key j are one contiguous range [j, qend):
+// the rest of the group for a prompt key (every response reads the whole
+// prompt), the rest of its own response otherwise.
+// The query-row launch writes D to `delta`; the key-row launch reads it.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_rowwise_dq_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ o, const float* __restrict__ lse, const T* __restrict__ dout,
+    T* __restrict__ dq, float* __restrict__ delta, const int32_t* __restrict__ g0a,
+    const int32_t* __restrict__ pea, const int32_t* __restrict__ ssa, int32_t Ttok, int32_t Hq,
+    int32_t Hkv, float c_log2, float scale) {
+  constexpr int E = D / 64;
+  const int64_t idx = blockIdx.x;
+  const int32_t t = int32_t(idx / Hq);
+  const int32_t h = int32_t(idx % Hq);
+  const int32_t hk = h / (Hq / Hkv);
+  const int lane = threadIdx.x;
+  const int64_t row = (int64_t(t) * Hq + h) * D;
+  float qv[E], gv[E], acc[E];
+  float dd = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qv[e] = to_f<T>(q[row + lane * E + e]);
+    gv[e] = to_f<T>(dout[row + lane * E + e]);
+    dd += gv[e] * to_f<T>(o[row + lane * E + e]);
+    acc[e] = 0.f;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dd += __shfl_xor(dd, off, 64);
+  const float l2 = lse[int64_t(h) * Ttok + t] * 1.44269504088896340736f;
+  const int32_t g0 = g0a[t], pe = pea[t], ss = ssa[t];
+  for (int32_t j = g0; j <= t; ++j) {
+    if (j >= pe && j < ss) j = ss;   // skip sibling suffixes (ss <= t always)
+    const int64_t kv = (int64_t(j) * Hkv + hk) * D;
+    float sp = 0.f, dp = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sp += qv[e] * to_f<T>(k[kv + lane * E + e]);
+      dp += gv[e] * to_f<T>(v[kv + lane * E + e]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      sp += __shfl_xor(sp, off, 64);
+      dp += __shfl_xor(dp, off, 64);
+    }
+    const float ds = exp2f(sp * c_log2 - l2) * (dp - dd);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += ds * to_f<T>(k[kv + lane * E + e]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) dq[row + lane * E + e] = from_f<T>(acc[e] * scale);
+  if (lane == 0) delta[int64_t(h) * Ttok + t] = dd;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_rowwise_dkv_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ lse, const float* __restrict__ delta, const T* __restrict__ dout,
+    T* __restrict__ dk, T* __restrict__ dv, const int32_t* __restrict__ pea,
+    const int32_t* __restrict__ ssa, const int32_t* __restrict__ owner,
+    const int32_t* __restrict__ group_off, const int32_t* __restrict__ suffix_lens,
+    int32_t Ttok, int32_t Hq, int32_t Hkv, float c_log2, float scale) {
+  constexpr int E = D / 64;
+  const int64_t idx = blockIdx.x;
+  const int32_t j = int32_t(idx / Hkv);
+  const int32_t hk = int32_t(idx % Hkv);
+  const int32_t r = Hq / Hkv;
+  const int lane = threadIdx.x;
+  const int64_t kv = (int64_t(j) * Hkv + hk) * D;
+  float kvk[E], kvv[E], ak[E], av[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kvk[e] = to_f<T>(k[kv + lane * E + e]);
+    kvv[e] = to_f<T>(v[kv + lane * E + e]);
+    ak[e] = 0.f;
+    av[e] = 0.f;
+  }
+  // owner: the group of a prompt token, the response of a response token
+  const int32_t qend =
+      j < pea[j] ? group_off[owner[j] + 1] : ssa[j] + suffix_lens[owner[j]];
+  for (int32_t t = j; t < qend; ++t) {
+    for (int32_t h = hk * r; h < hk * r + r; ++h) {
+      const int64_t row = (int64_t(t) * Hq + h) * D;
+      float qv[E], gv[E];
+      float sp = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        qv[e] = to_f<T>(q[row + lane * E + e]);
+        gv[e] = to_f<T>(dout[row + lane * E + e]);
+        sp += qv[e] * kvk[e];
+        dp += gv[e] * kvv[e];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        sp += __shfl_xor(sp, off, 64);
+        dp += __shfl_xor(dp, off, 64);
+      }
+      const int64_t hr = int64_t(h) * Ttok + t;
+      const float p = exp2f(sp * c_log2 - lse[hr] * 1.44269504088896340736f);
+      const float ds = p * (dp - delta[hr]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        av[e] += p * gv[e];
+        ak[e] += ds * qv[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    dk[kv + lane * E + e] = from_f<T>(ak[e] * scale);
+    dv[kv + lane * E + e] = from_f<T>(av[e]);
+  }
+}
+
 // Decode step, one workgroup (one wave) per (response k, query head h): the
 // newest token of response k against its group's prompt rows and its first
 // len_k = clamp(cur_lens[k], 0, capacity_k) own rows (PackInfer abstract,
@@ -407,6 +530,36 @@ hipError_t pg_launch_rope(const pg_layout& L, const int64_t* pos, const void* q_
     if (L.d == 128) PG_ROPE(float, 128); else PG_ROPE(float, 64);
   }
 #undef PG_ROPE
+  return hipGetLastError();
+}
+
+hipError_t pg_launch_bwd_rowwise(const pg_layout& L, const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, float* delta, pg_dtype dtype,
+                                 float softmax_scale, hipStream_t stream) {
+  const int64_t qrows = L.T * L.Hq, krows = L.T * L.Hkv;
+  if (qrows > int64_t(0x7fffffff)) return hipErrorInvalidConfiguration;
+  if (qrows == 0) return hipSuccess;
+  const float c = softmax_scale * 1.44269504088896340736f;
+  const int32_t T = int32_t(L.T);
+#define PG_BWD(TY, DD)                                                                          \
+  do {                                                                                          \
+    bwd_rowwise_dq_kernel<TY, DD><<<dim3(uint32_t(qrows)), dim3(64), 0, stream>>>(              \
+        static_cast<const TY*>(q), static_cast<const TY*>(k), static_cast<const TY*>(v),         \
+        static_cast<const TY*>(o), lse, static_cast<const TY*>(dout), static_cast<TY*>(dq),      \
+        delta, L.d_g0, L.d_pe, L.d_ss, T, L.Hq, L.Hkv, c, softmax_scale);                        \
+    bwd_rowwise_dkv_kernel<TY, DD><<<dim3(uint32_t(krows)), dim3(64), 0, stream>>>(             \
+        static_cast<const TY*>(q), static_cast<const TY*>(k), static_cast<const TY*>(v), lse,    \
+        delta, static_cast<const TY*>(dout), static_cast<TY*>(dk), static_cast<TY*>(dv),         \
+        L.d_pe, L.d_ss, L.d_owner, L.d_group_off, L.d_suffix_lens, T, L.Hq, L.Hkv, c,            \
+        softmax_scale);                                                                         \
+  } while (0)
+  if (dtype == PG_BF16) {
+    if (L.d == 128) PG_BWD(uint16_t, 128); else PG_BWD(uint16_t, 64);
+  } else {
+    if (L.d == 128) PG_BWD(float, 128); else PG_BWD(float, 64);
+  }
+#undef PG_BWD
   return hipGetLastError();
 }
 

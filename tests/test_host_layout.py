@@ -307,7 +307,9 @@ def test_backward_work_list_on_dpo_workload():
     _check_kv_invariants(L, w.prefix_lens.tolist(), [s for _, s in w.groups()], 32, 8)
 
 
-def test_backward_needs_bf16_d128_and_an_uploaded_layout():
+def test_backward_needs_an_uploaded_layout():
+    """Every dtype and head size has a backward (bf16 d = 128 on the MFMA
+    kernels, the rest per row); without a device copy the call is refused."""
     lib = _lib.load()
     L = _build([5], [[3]], hq=4, hkv=1, d=64)
     dummy = ctypes.c_void_p(16)
