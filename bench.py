@@ -56,6 +56,237 @@ def load_traffic(workload: str):
     return r.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------ rocprofv3 summaries --
+# `--profile-recipe` prints the rocprofv3 runs of this script behind each
+# summary under profiles/ (run from the repository root after
+# `export TMPDIR=/tmp`); `--profile-summary` turns their CSV output into the
+# markdown, and with --record-traffic stores the attention kernel's calibrated
+# HBM bytes per launch in profiles/attn_traffic.json under the current kernel
+# source hash. Both take the same --workload and --profile-dir.
+
+COPY_BYTES = 1 << 30
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_IDX_ACTIVE",
+               "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+               "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_TRANS_F32", "GRBM_GUI_ACTIVE"]
+TCC_COUNTERS = ["TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE"]
+TRACE_STEPS, TRACE_WARMUP = 10, 3
+
+
+def profile_recipe(workload: int, root: str):
+    """(name, output directory, command) of every run behind one summary."""
+    tag = f"wl{workload}"
+    run = f"python3 bench.py --no-cpu-baseline --no-unpacked --workload {workload}"
+    fwd_only = run + " --no-backward --no-gathers --no-decode --steps 2 --warmup 1"
+    d = lambda name: os.path.join(root, name)
+    pmc = lambda counters, out, prog, limit=150: (
+        f"timeout -s KILL {limit} rocprofv3 --pmc {' '.join(counters)} -d {out} -o pmc "
+        f"--output-format csv -- {prog}")
+    copy = f"python3 bench.py --copy-bytes {COPY_BYTES}"
+    return [
+        ("trace", d(f"{tag}_trace"),
+         f"timeout -s KILL 300 rocprofv3 --kernel-trace --stats -d {d(f'{tag}_trace')} -o trace "
+         "--output-format csv -- "
+         f"{run} --steps {TRACE_STEPS} --warmup {TRACE_WARMUP}"),
+        ("fetch", d(f"{tag}_fetch"), pmc(["FETCH_SIZE"], d(f"{tag}_fetch"), run + " --steps 3 --warmup 1")),
+        ("write", d(f"{tag}_write"), pmc(["WRITE_SIZE"], d(f"{tag}_write"), run + " --steps 3 --warmup 1")),
+        ("cal_fetch", d("copy_fetch"), pmc(["FETCH_SIZE"], d("copy_fetch"), copy, 60)),
+        ("cal_write", d("copy_write"), pmc(["WRITE_SIZE"], d("copy_write"), copy, 60)),
+        ("sq", d(f"{tag}_sq"), pmc(SQ_COUNTERS, d(f"{tag}_sq"), fwd_only)),
+        ("tcc", d(f"{tag}_tcc"), pmc(TCC_COUNTERS, d(f"{tag}_tcc"), fwd_only)),
+    ]
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not paths:
+        raise SystemExit(f"bench.py: no *{suffix} under {directory}")
+    for path in paths:
+        with open(path, newline="") as f:
+            yield from csv.DictReader(f)
+
+
+def _short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    depth, cut = 0, len(name)
+    for i in range(len(name) - 1, -1, -1):   # drop the trailing argument list
+        if name[i] == ")":
+            depth += 1
+        elif name[i] == "(":
+            depth -= 1
+            if depth == 0:
+                cut = i
+                break
+    return name[:cut].strip()[:60]
+
+
+def _kernel_durations(trace_dir: str):
+    """Kernel name -> dispatch durations in us, in launch order."""
+    rows = [r for r in _csv_rows(trace_dir, "kernel_trace.csv")]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = {}
+    for r in rows:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        out.setdefault(_short_name(r["Kernel_Name"]), []).append(dur)
+    return out
+
+
+def _counter_medians(pmc_dir: str):
+    """Kernel name -> counter name -> median over dispatches of the per-dispatch sum."""
+    import statistics
+    per = {}
+    for r in _csv_rows(pmc_dir, "counter_collection.csv"):
+        key = (_short_name(r["Kernel_Name"]), r["Counter_Name"])
+        d = per.setdefault(key, {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (k, c), vals in per.items():
+        out.setdefault(k, {})[c] = statistics.median(vals.values())
+    return out
+
+
+def _algorithmic_bytes(kernel: str, T: int, Hq: int, Hkv: int, d: int):
+    """Compulsory HBM bytes of one launch: every tensor the kernel must touch, once."""
+    q = T * Hq * d * 2            # one [T, Hq, d] bf16 tensor
+    kv = T * Hkv * d * 2          # one [T, Hkv, d] bf16 tensor
+    row = T * Hq * 4              # one fp32 value per (token, query head)
+    table = {
+        "positions_kernel": T * 8,
+        "rope_kernel<bf16,128>": 2 * (q + kv) + T * 8,
+        "attn_fwd_bf16_d128": 2 * q + 2 * kv + row,          # Q, K, V in; O, lse out
+        "bwd_dq_kernel": 4 * q + 2 * kv + 2 * row,            # Q, dO, O, K, V, lse in; dQ, D out
+        "bwd_dkv_kernel": 2 * q + 4 * kv + 2 * row,           # Q, dO, K, V, lse, D in; dK, dV out
+    }
+    return table.get(kernel)
+
+
+def profile_summary(args) -> int:
+    """Markdown summary of the runs `profile_recipe` lists (see the comment above)."""
+    import numpy as np
+    from workloads import make_workload
+    import shared_prefix_packed_amd as pg
+    recipe = {name: (out, cmd) for name, out, cmd in profile_recipe(args.workload, args.profile_dir)}
+    w = make_workload(args.workload)
+    L = pg.pg_build_layout_host(w.prefix_lens, w.suffix_counts, w.suffix_lens, w.num_q_heads,
+                                w.num_kv_heads, w.head_dim, w.rope_theta)
+    pairs = int(L.summary().useful_pairs)
+    L.close()
+    T, Hq, Hkv, d = w.total_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim
+    fwd_flop = 4 * d * Hq * pairs
+    attn = "attn_fwd_bf16_d128"
+    lines = [f"# rocprofv3 summary: {w.name} (T={T}, {w.num_groups} groups, Hq={Hq}, Hkv={Hkv}, d={d})", "",
+             "Every command runs from the repository root after `export TMPDIR=/tmp`; "
+             f"`python3 bench.py --profile-summary --workload {args.workload} --record-traffic` "
+             "then writes this file from their output (and the attention entry of "
+             "profiles/attn_traffic.json).", "",
+             "Kernel trace:", "", "    " + recipe["trace"][1], "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    durs = _kernel_durations(recipe["trace"][0])
+    total = sum(sum(v) for v in durs.values())
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {len(v)} | {np.mean(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{100 * sum(v) / total:.1f} |")
+    a = durs.get(attn, [])
+    timed = a[TRACE_WARMUP:TRACE_WARMUP + TRACE_STEPS]
+    if timed:
+        t_us = float(np.mean(timed))
+        tf = fwd_flop / (t_us * 1e-6) / 1e12
+        lines += ["", f"{attn}: {len(a)} launches = {TRACE_WARMUP} warm-up + {len(timed)} timed steps. "
+                  f"Over the timed steps: mean {t_us:.1f} us, median {float(np.median(timed)):.1f} us; "
+                  f"{fwd_flop} useful FLOP per launch (4 d Hq x {pairs} allowed pairs) / {t_us:.1f} us = "
+                  f"{tf:.1f} TFLOP/s = {100 * tf / PEAK_BF16_TFLOPS:.1f} % of the "
+                  f"{PEAK_BF16_TFLOPS} TFLOP/s dense bf16 peak (bench.py's `roofline.achieved` is the "
+                  f"HIP-event mean of the same timed launches)."]
+    bwd_q, bwd_kv = durs.get("bwd_dq_kernel"), durs.get("bwd_dkv_kernel")
+    if bwd_q and bwd_kv:
+        bq, bk = float(np.mean(bwd_q[2:] or bwd_q)), float(np.mean(bwd_kv[2:] or bwd_kv))
+        bflop = 10 * d * Hq * pairs
+        lines += ["", f"Backward (pg_attn_bwd after the forward steps, its 2 warm-up calls left out): dQ "
+                  f"{bq:.1f} us + dK/dV {bk:.1f} us = {bq + bk:.1f} us for {bflop} useful FLOP "
+                  f"(10 d Hq per allowed pair) = {bflop / ((bq + bk) * 1e-6) / 1e12:.1f} TFLOP/s = "
+                  f"{100 * bflop / ((bq + bk) * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f} % of peak; dQ kernel "
+                  f"alone {0.6 * bflop / (bq * 1e-6) / 1e12:.1f} TFLOP/s (S, dP, dQ), dK/dV kernel alone "
+                  f"{0.8 * bflop / (bk * 1e-6) / 1e12:.1f} TFLOP/s (S, dP, dV, dK)."]
+
+    fetch, write = _counter_medians(recipe["fetch"][0]), _counter_medians(recipe["write"][0])
+    cf, cw = _counter_medians(recipe["cal_fetch"][0]), _counter_medians(recipe["cal_write"][0])
+    copy_kib = COPY_BYTES / 1024.0
+
+    def cal(meds, counter):
+        vals = [c[counter] for c in meds.values() if counter in c]
+        v = max(vals) if vals else 0.0   # the copy is the largest dispatch of its run
+        return copy_kib / v if v else float("nan")
+    ff, fw = cal(cf, "FETCH_SIZE"), cal(cw, "WRITE_SIZE")
+    lines += ["", "HBM traffic, one counter per run, then the same two passes over a plain device copy:", ""]
+    lines += ["    " + recipe[n][1] for n in ("fetch", "write", "cal_fetch", "cal_write")]
+    lines += ["", f"Calibration: the {COPY_BYTES}-byte copy reads FETCH_SIZE "
+              f"{copy_kib / ff:.0f} KiB and WRITE_SIZE {copy_kib / fw:.0f} KiB, so bytes = FETCH_SIZE x 1024 x "
+              f"{ff:.3f} and WRITE_SIZE x 1024 x {fw:.3f}.", "",
+              "| kernel | FETCH KiB (median) | WRITE KiB (median) | HBM MB/launch (calibrated) | algorithmic MB | ratio |",
+              "|---|---|---|---|---|---|"]
+    attn_bytes = None
+    for k in sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, {}).get("FETCH_SIZE", 0))):
+        fk, wk = fetch.get(k, {}).get("FETCH_SIZE", 0.0), write.get(k, {}).get("WRITE_SIZE", 0.0)
+        hbm = (fk * ff + wk * fw) * 1024
+        alg = _algorithmic_bytes(k, T, Hq, Hkv, d)
+        if k == attn:
+            attn_bytes = int(round(hbm))
+        lines.append(f"| {k} | {fk:.0f} | {wk:.0f} | {hbm / 1e6:.1f} | "
+                     f"{'' if alg is None else f'{alg / 1e6:.1f}'} | {'' if alg is None else f'{hbm / alg:.2f}'} |")
+    lines += ["", "Algorithmic bytes: each tensor a kernel must read or write, once (attention: Q, K, V in, "
+              "O and lse out; dQ launch: Q, dO, O, K, V, lse in, dQ and D out; dK/dV launch: Q, dO, K, V, "
+              "lse, D in, dK and dV out). The excess is K/V (forward, dQ) or Q/dO (dK/dV) re-read by the "
+              "work items of a group, which L2 serves only in part."]
+
+    meds = {}
+    for n in ("sq", "tcc"):
+        if os.path.isdir(recipe[n][0]):
+            meds.update(_counter_medians(recipe[n][0]).get(attn, {}))
+    if meds:
+        lines += ["", f"Counters of {attn} (medians over its dispatches, one run per pass):", "",
+                  "    " + recipe["sq"][1], "    " + recipe["tcc"][1], "",
+                  "| counter | value |", "|---|---|"]
+        for c, v in sorted(meds.items()):
+            lines.append(f"| {c} | {v:.0f} |")
+        gui = meds.get("GRBM_GUI_ACTIVE")
+        if gui:
+            simd_cycles = gui / 8 * 1024   # GRBM_GUI_ACTIVE sums the 8 XCDs; 1024 SIMDs
+            derived = []
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in meds:
+                derived.append(f"MFMA busy {100 * meds['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.1f} %")
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in meds:
+                derived.append("MFMA and VALU issuing together "
+                               f"{100 * meds['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd_cycles:.1f} %")
+            if meds.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in meds:
+                derived.append("LDS bank conflicts "
+                               f"{100 * meds['SQ_LDS_BANK_CONFLICT'] / meds['SQ_LDS_IDX_ACTIVE']:.1f} % of LDS cycles")
+            if "TCC_HIT_sum" in meds and meds.get("TCC_HIT_sum", 0) + meds.get("TCC_MISS_sum", 0) > 0:
+                derived.append("L2 hit rate "
+                               f"{100 * meds['TCC_HIT_sum'] / (meds['TCC_HIT_sum'] + meds['TCC_MISS_sum']):.1f} %")
+            if timed:
+                derived.append(f"clock {gui / 8 / (float(np.median(timed)) * 1e-6) / 1e9:.2f} GHz "
+                               "(GRBM_GUI_ACTIVE per XCD over the median timed launch)")
+            lines += ["", "Derived (SIMD cycles = GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): " +
+                      "; ".join(derived) + "."]
+    print("\n".join(lines))
+
+    if args.record_traffic and attn_bytes:
+        try:
+            with open(TRAFFIC_FILE) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            rec = {}
+        rec[w.name] = {"kernel_hash": kernel_source_hash(), "hbm_bytes_per_launch": attn_bytes,
+                       "fetch_kib": fetch.get(attn, {}).get("FETCH_SIZE"),
+                       "write_kib": write.get(attn, {}).get("WRITE_SIZE"),
+                       "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    return 0
+
+
 def cpu_baseline(w, qkv, budget_s: float):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
     whole groups, one query head at a time (group-major), until the time
@@ -124,7 +355,23 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against a known byte count)")
+    ap.add_argument("--profile-recipe", action="store_true",
+                    help="no GPU work: print the rocprofv3 runs behind the --workload's profile summary")
+    ap.add_argument("--profile-summary", action="store_true",
+                    help="no GPU work: write the --workload's profile summary (markdown, stdout) from "
+                         "the output of the --profile-recipe runs")
+    ap.add_argument("--profile-dir", default="gpurun_out/prof",
+                    help="where the --profile-recipe runs write (default gpurun_out/prof)")
+    ap.add_argument("--record-traffic", action="store_true",
+                    help="with --profile-summary: store the attention launch's calibrated HBM bytes in "
+                         "profiles/attn_traffic.json under the current kernel source hash")
     args = ap.parse_args(argv)
+    if args.profile_recipe:
+        for _, _, cmd in profile_recipe(args.workload, args.profile_dir):
+            print(cmd)
+        return 0
+    if args.profile_summary:
+        return profile_summary(args)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
