@@ -146,19 +146,20 @@ def _counter_medians(pmc_dir: str):
     return out
 
 
-def _algorithmic_bytes(kernel: str, T: int, Hq: int, Hkv: int, d: int):
+def _algorithmic_bytes(kernel: str, T: int, Hq: int, Hkv: int, d: int, elem: int):
     """Compulsory HBM bytes of one launch: every tensor the kernel must touch, once."""
-    q = T * Hq * d * 2            # one [T, Hq, d] bf16 tensor
-    kv = T * Hkv * d * 2          # one [T, Hkv, d] bf16 tensor
+    q = T * Hq * d * elem         # one [T, Hq, d] tensor
+    kv = T * Hkv * d * elem       # one [T, Hkv, d] tensor
     row = T * Hq * 4              # one fp32 value per (token, query head)
     table = {
-        "positions_kernel": T * 8,
-        "rope_kernel<bf16,128>": 2 * (q + kv) + T * 8,
-        "attn_fwd_bf16_d128": 2 * q + 2 * kv + row,          # Q, K, V in; O, lse out
-        "bwd_dq_kernel": 4 * q + 2 * kv + 2 * row,            # Q, dO, O, K, V, lse in; dQ, D out
-        "bwd_dkv_kernel": 2 * q + 4 * kv + 2 * row,           # Q, dO, K, V, lse, D in; dK, dV out
+        "positions_kernel": T * 3 * 4 + T * 8,                # g0, pe, ss per token in; int64 out
+        "rope_kernel": 2 * (q + kv) + T * 8,                   # Q, K, positions in; Q, K out
+        "attn_fwd_bf16_d128": 2 * q + 2 * kv + row,            # Q, K, V in; O, lse out
+        "bwd_dq_kernel": 4 * q + 2 * kv + 2 * row,             # Q, dO, O, K, V, lse in; dQ, D out
+        "bwd_dkv_kernel": 2 * q + 4 * kv + 2 * row,            # Q, dO, K, V, lse, D in; dK, dV out
     }
-    return table.get(kernel)
+    base = kernel[5:] if kernel.startswith("void ") else kernel
+    return table.get(base.split("<")[0])
 
 
 def profile_summary(args) -> int:
@@ -229,15 +230,16 @@ def profile_summary(args) -> int:
     for k in sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, {}).get("FETCH_SIZE", 0))):
         fk, wk = fetch.get(k, {}).get("FETCH_SIZE", 0.0), write.get(k, {}).get("WRITE_SIZE", 0.0)
         hbm = (fk * ff + wk * fw) * 1024
-        alg = _algorithmic_bytes(k, T, Hq, Hkv, d)
+        alg = _algorithmic_bytes(k, T, Hq, Hkv, d, 2 if w.dtype == "bf16" else 4)
         if k == attn:
             attn_bytes = int(round(hbm))
         lines.append(f"| {k} | {fk:.0f} | {wk:.0f} | {hbm / 1e6:.1f} | "
                      f"{'' if alg is None else f'{alg / 1e6:.1f}'} | {'' if alg is None else f'{hbm / alg:.2f}'} |")
-    lines += ["", "Algorithmic bytes: each tensor a kernel must read or write, once (attention: Q, K, V in, "
-              "O and lse out; dQ launch: Q, dO, O, K, V, lse in, dQ and D out; dK/dV launch: Q, dO, K, V, "
-              "lse, D in, dK and dV out). The excess is K/V (forward, dQ) or Q/dO (dK/dV) re-read by the "
-              "work items of a group, which L2 serves only in part."]
+    lines += ["", "Algorithmic bytes: each tensor a kernel must read or write, once (positions: three "
+              "per-token tables in, int64 positions out; RoPE: Q, K, positions in, Q, K out; attention: "
+              "Q, K, V in, O and lse out; dQ launch: Q, dO, O, K, V, lse in, dQ and D out; dK/dV launch: "
+              "Q, dO, K, V, lse, D in, dK and dV out). The excess is K/V (forward, dQ) or Q/dO (dK/dV) "
+              "re-read by the work items of a group, which L2 serves only in part."]
 
     meds = {}
     for n in ("sq", "tcc"):
