@@ -156,11 +156,6 @@ struct SpanTiles {
     k1 = ld_scalar(spans, 2 * s + 1);
     ka = k0;
   }
-  __device__ void init(const pg_key_span* spans, int s0, int n) {
-    s = __builtin_amdgcn_readfirstlane(s0);
-    s_end = __builtin_amdgcn_readfirstlane(s0 + n);
-    load(spans);
-  }
   __device__ void next(const pg_key_span* spans) {
     ka += Q_KT;
     if (ka >= k1 && ++s < s_end) load(spans);
@@ -170,7 +165,22 @@ struct SpanTiles {
 __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Q_NSTAGE * Q_STAGE];
 
-  const pg_work_item it = a.items[blockIdx.x];
+  pg_work_item it;
+  {
+    const __attribute__((address_space(4))) int* c =
+        (const __attribute__((address_space(4))) int*)(a.items + blockIdx.x);
+    it.t0 = c[0];
+    it.t1 = c[1];
+    it.hq0 = c[2];
+    it.pe = c[3];
+    it.span0 = c[4];
+    it.nspan = c[5];
+    it.ntiles = c[6];
+    it.k0 = c[7];
+    it.k1 = c[8];
+  }
+  asm volatile("" ::"s"(it.t0), "s"(it.t1), "s"(it.hq0), "s"(it.pe), "s"(it.span0),
+               "s"(it.nspan), "s"(it.ntiles), "s"(it.k0), "s"(it.k1));
   if (it.nspan == 0) return;   // padding of a shorter XCD queue
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,31 +195,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   const bool wave_active = tb < te;
   const int tq = wave_active ? min(tb + qi, te - 1) : it.t0;
   const bool row_valid = wave_active && (tb + qi < te);
-
-  // Q and dO rows as B operands (lane: query qi, d = 16 ks + 8 half + 0..7)
-  bf16x8_t qf[8], dof[8];
-  {
-    const int64_t base = (int64_t(tq) * a.Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = as_bf16x8(ldg16(a.q + base + 16 * ks));
-      dof[ks] = as_bf16x8(ldg16(a.dout + base + 16 * ks));
-    }
-  }
-  float lse2 = a.lse[int64_t(h) * a.T + tq] * LOG2E;
-  float dlt = 0.f;
-  int ss_t = a.tok_ss[tq];
-  // Redefine the loaded values by an empty asm: the compiler waits for their
-  // loads once, here. Counted inside the tile loop instead, next to the tile
-  // fetches it cannot see, its waits would drain every tile in flight.
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qf[ks]), "+v"(dof[ks]));
-  asm volatile("" : "+v"(lse2), "+v"(dlt), "+v"(ss_t));
-  const int ss_max = ld_scalar(a.tok_ss, wave_active ? te - 1 : it.t0);
-
-  int ntiles = 0;
-  for (int s = it.span0; s < it.span0 + it.nspan; ++s)
-    ntiles += (ld_scalar(a.spans, 2 * s + 1) - ld_scalar(a.spans, 2 * s) + Q_KT - 1) / Q_KT;
 
   // staging: waves 0-3 bring K (blocks 4 w + i), waves 4-7 V
   const int w4 = wave & 3;
@@ -234,6 +219,43 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int i = 0; i < Q_LOADS; ++i) buf16_to_lds(rs, goff[i], sb + ldst[i]);
   };
 
+  // The first two tile fetches go out before anything else, from the item's
+  // own copy of its first span (no span-list read before them); Q, dO, lse,
+  // the segment starts and O (for D) load while they are in flight.
+  const int ntiles = __builtin_amdgcn_readfirstlane(it.ntiles);
+  SpanTiles ld;
+  ld.s = __builtin_amdgcn_readfirstlane(it.span0);
+  ld.s_end = __builtin_amdgcn_readfirstlane(it.span0 + it.nspan);
+  ld.k0 = __builtin_amdgcn_readfirstlane(it.k0);
+  ld.k1 = __builtin_amdgcn_readfirstlane(it.k1);
+  ld.ka = ld.k0;
+  for (int n = 0; n < 2 && n < ntiles; ++n) {
+    fetch(ld.ka, ld.k1, n);
+    ld.next(a.spans);
+  }
+
+  // Q and dO rows as B operands (lane: query qi, d = 16 ks + 8 half + 0..7)
+  bf16x8_t qf[8], dof[8];
+  {
+    const int64_t base = (int64_t(tq) * a.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = as_bf16x8(ldg16(a.q + base + 16 * ks));
+      dof[ks] = as_bf16x8(ldg16(a.dout + base + 16 * ks));
+    }
+  }
+  float lse2 = a.lse[int64_t(h) * a.T + tq] * LOG2E;
+  float dlt = 0.f;
+  int ss_t = a.tok_ss[tq];
+  // Redefine the loaded values by an empty asm: the compiler waits for their
+  // loads once, here. Counted inside the tile loop instead, next to the tile
+  // fetches it cannot see, its waits would drain every tile in flight.
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qf[ks]), "+v"(dof[ks]));
+  asm volatile("" : "+v"(lse2), "+v"(dlt), "+v"(ss_t));
+  const int ss_max = ld_scalar(a.tok_ss, wave_active ? te - 1 : it.t0);
+
+
   // A operand reads: row-major K/V row 32 kb + qi, chunk 2 ks + half (swizzled)
   int koff[8];
 #pragma unroll
@@ -246,13 +268,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  SpanTiles ld, cp;
-  ld.init(a.spans, it.span0, it.nspan);
-  for (int n = 0; n < 2 && n < ntiles; ++n) {
-    fetch(ld.ka, ld.k1, n);
-    ld.next(a.spans);
-  }
-  cp.init(a.spans, it.span0, it.nspan);
+  SpanTiles cp;
+  cp.s = ld.s_end - it.nspan;
+  cp.s_end = ld.s_end;
+  cp.k0 = __builtin_amdgcn_readfirstlane(it.k0);
+  cp.k1 = __builtin_amdgcn_readfirstlane(it.k1);
+  cp.ka = cp.k0;
   // D = sum_d dO O of this row in fp32: each half of the wave holds half of d.
   // The items cover every (token, head) row once, so D is complete for the
   // dK/dV launch that follows. Formed after the first tile fetches are issued,
@@ -311,15 +332,32 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   // P^T and dS^T; register i of block kb holds key ka + 32 kb + 8 (i/4) + 4 half + i%4
   auto second_half = [&](const unsigned char* st, bool full, int lo, int hi) {
+    float p[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = 32 * kb + 8 * (i >> 2) + (i & 3);
-        float p = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -lse2));
-        if (!full) p = (c >= lo && c <= hi) ? p : 0.f;
-        sacc[kb][i] = p * (pacc[kb][i] - dlt);
+      for (int i = 0; i < 16; ++i) p[kb][i] = fast_exp2(fmaf(sacc[kb][i], a.c_log2, -lse2));
+    if (!full) {
+      asm volatile("" ::: "memory");
+      // keys of the tile this lane's row reads: offsets [lo, hi] as a 64-bit
+      // mask; each p takes its bit by a signed bitfield extract and an AND
+      const int l0 = max(lo, 0), h0 = min(hi, 63);
+      const uint64_t ones = ~uint64_t(0);
+      const uint64_t M = h0 < l0 ? uint64_t(0) : ((ones >> (63 - h0)) & (ones << l0));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t w = uint32_t(M >> (32 * kb));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int keep = __builtin_amdgcn_sbfe(int(w), 8 * (i >> 2) + (i & 3), 1);
+          p[kb][i] = __int_as_float(__float_as_int(p[kb][i]) & keep);
+        }
       }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = p[kb][i] * (pacc[kb][i] - dlt);
     bf16x8_t dsf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) dsf[ks] = pack_step(sacc[ks >> 1], ks);
