@@ -453,7 +453,8 @@ static_assert((KV_WAVES / 2) * 32 == PG_KV_BLOCK, "key block = 4 slices x 32 key
 // with the P of their slice's dV wave. Each role runs its own loop and holds
 // only its own operands and accumulators, so two waves fit on a SIMD (waves w
 // and w + 4 share one) and hide each other's latency. Both loops take the
-// same barriers: one when a tile's stage has landed, one when P is in LDS.
+// same barrier, one per tile, between the two halves of a tile: P of the
+// tile is in LDS and the next tile's stage has landed.
 struct KvCtx {
   const pg_kv_item* it;
   int lane, wave, col, half, hk, kw0, kw1, key, q_start, nq, ntiles, q_row_bytes;
@@ -482,10 +483,22 @@ __device__ inline void kv_fetch(const BwdArgs& a, const KvCtx& c, int n, int sta
   buf4_to_lds(rl, 4 * c.lane, c.lds_base + uint32_t(stage * KV_STAGE) + KV_ROWS + 256 * min(c.wave, 2));
 }
 
-// P of one (query tile, slice) in fp32, as the dV waves hand it to the dK
-// waves: float4 m (= 4 kb + g) of lane l at byte 1024 m + 16 l.
+// P of one (query tile, slice) in fp16, as the dV waves hand it to the dK
+// waves: the four values of accumulator group m (= 4 kb + g) of lane l at
+// byte 512 m + 8 l of the slice's 4 KB; two buffers, for even and odd tiles.
 constexpr int KV_PX = KV_NSTAGE * KV_STAGE;
-constexpr int KV_SMEM = KV_PX + 4 * 8192;
+constexpr int KV_PBUF = 4 * 4096;
+constexpr int KV_SMEM = KV_PX + 2 * KV_PBUF;
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// nearest-even fp32 -> fp16 of two values (one v_cvt_pk_f16_f32)
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+  f16x2_t v;
+  v.x = static_cast<_Float16>(a);
+  v.y = static_cast<_Float16>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // P = exp(S scale - lse) of the 64 x 32 tile in the accumulator layout, zero
 // where the row cannot read the key (only on tiles crossing the diagonal or
@@ -535,7 +548,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) aoff[ks] = c.col * 256 + 16 * ((2 * ks + c.half) ^ rm_swz(c.col));
   const TrOffsets tro(c.lane);
-  float4* const px = reinterpret_cast<float4*>(smem + KV_PX + 8192 * (c.wave & 3)) + c.lane;
+  uint2* const px = reinterpret_cast<uint2*>(smem + KV_PX + 4096 * (c.wave & 3)) + c.lane;
 
   f32x16_t acc[4];   // dV or dK: rows = keys (registers), lanes = d
 #pragma unroll
@@ -543,15 +556,16 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  if (c.ntiles > 1) kv_fetch(a, c, 1, 1);
+  if (c.ntiles > 1) {
+    kv_fetch(a, c, 1, 1);
+    wait_vmem<KV_LOADS>();
+  } else {
+    wait_vmem<0>();
+  }
+  bare_barrier();   // tile 0 has landed
 
   for (int n = 0; n < c.ntiles; ++n) {
-    if (n + 1 < c.ntiles)
-      wait_vmem<KV_LOADS>();
-    else
-      wait_vmem<0>();
-    bare_barrier();
-    if (n + 2 < c.ntiles) kv_fetch(a, c, n + 2, (n + 2) % KV_NSTAGE);
+    uint2* const pb = px + (n & 1) * (KV_PBUF / 8);
     const int q0 = c.q_start + KV_QT * (c.nq - 1 - n / a.r);
     // the slice has keys, and some row of the tile can read one of them
     const bool active = c.wave_keys && q0 + KV_QT - 1 >= c.kw0;
@@ -592,8 +606,8 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
           tile_p<true>(sacc, r4, a.c_log2, q0, c.half, c.key, it.qend);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
-          px[64 * m] = make_float4(sacc[m >> 2][4 * (m & 3)], sacc[m >> 2][4 * (m & 3) + 1],
-                                   sacc[m >> 2][4 * (m & 3) + 2], sacc[m >> 2][4 * (m & 3) + 3]);
+          pb[64 * m] = make_uint2(pack_f16x2(sacc[m >> 2][4 * (m & 3)], sacc[m >> 2][4 * (m & 3) + 1]),
+                                  pack_f16x2(sacc[m >> 2][4 * (m & 3) + 2], sacc[m >> 2][4 * (m & 3) + 3]));
       } else {
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -601,9 +615,15 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
           for (int j = 0; j < 4; ++j) sacc[m >> 2][4 * (m & 3) + j] -= (&r4[m].x)[j];
       }
     }
-    // P is written before any dK wave reads it
+    // One barrier per tile. Before it: this wave's part of tile n + 1 has
+    // landed (the only fetch in flight) and the dV wave's P is in LDS. After
+    // it, tile n + 2 goes to the stage of tile n - 1, whose last reads (the
+    // second half of n - 1) came before this barrier; P of tile n + 1 goes to
+    // the other buffer while the dK waves still read this one.
+    wait_vmem<0>();
     if constexpr (!KWAVE) wait_lds();
     bare_barrier();
+    if (n + 2 < c.ntiles) kv_fetch(a, c, n + 2, (n + 2) % KV_NSTAGE);
     if (!active) continue;
 
     // second half: dV += P^T dO, or dS = P (dP - D) and dK += dS^T Q (B by
@@ -611,9 +631,14 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
     if constexpr (KWAVE) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const float4 p4 = px[64 * m];
+        const uint2 p2 = pb[64 * m];
+        const f16x2_t lo = __builtin_bit_cast(f16x2_t, p2.x);
+        const f16x2_t hi = __builtin_bit_cast(f16x2_t, p2.y);
+        const float p4[4] = {float(lo.x), float(lo.y), float(hi.x), float(hi.y)};
+        // fma with a zero addend: one v_fma_mix_f32 straight from the fp16 P
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sacc[m >> 2][4 * (m & 3) + j] *= (&p4.x)[j];
+        for (int j = 0; j < 4; ++j)
+          sacc[m >> 2][4 * (m & 3) + j] = __builtin_fmaf(p4[j], sacc[m >> 2][4 * (m & 3) + j], 0.f);
       }
     }
     const unsigned char* bt = st + (KWAVE ? 0 : KV_REGION);
