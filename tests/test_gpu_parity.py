@@ -21,7 +21,7 @@ import torch
 import shared_prefix_packed_amd as pg
 from oracle import pg_oracle as O
 import oracle_units as U
-from workloads import bf16_bits_to_f32, draw_qkv, make_custom, make_workload
+from workloads import bf16_bits_to_f32, draw_qkv, f32_to_bf16_bits, make_custom, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -178,6 +178,45 @@ def test_rope_in_place_equals_out_of_place():
     torch.cuda.synchronize()
     assert torch.equal(q2.view(torch.int16), qr.view(torch.int16))
     assert torch.equal(k2.view(torch.int16), kr.view(torch.int16))
+
+
+def test_rope_near_cancellation():
+    """Rotations whose exact result nearly cancels: x = y tan(phi) rounded to
+    bf16 makes x cos - y sin a rounding residual of x, hundreds of times
+    smaller than the inputs (and -x / tan(phi) does the same to y cos + x sin
+    in the other heads). These are the cases where a rotation in plain fp32
+    misses the nearest bf16 by many ulps; the kernel must stay within one."""
+    w = make_custom([700, 0], [[300, 0, 450], [260]], num_q_heads=4, num_kv_heads=2)
+    L = layout_of(w)
+    pos = pg.pg_position_ids(L)
+    opos = O.positions(oracle_layout(w))
+    T, d = w.total_tokens, w.head_dim
+    half = d // 2
+    r = np.random.default_rng(11)
+    omega = w.rope_theta ** (-2.0 * np.arange(half) / d)
+    tan = np.tan(opos[:, None].astype(np.float64) * omega[None, :])[:, None, :]
+    ok = (np.abs(tan) <= 8.0) & (np.abs(tan) >= 1.0 / 8.0)
+
+    def make(H):
+        a = O.round_to_bf16(r.standard_normal((T, H, half)))
+        b = O.round_to_bf16(r.standard_normal((T, H, half)))
+        lo = np.where(ok, O.round_to_bf16(a * tan), b)     # lo x cos - hi sin ~ 0 (hi = a)
+        x = np.concatenate([lo, a], axis=-1)
+        hi = np.where(ok, O.round_to_bf16(-a * tan), b)    # hi x cos + lo sin ~ 0 (lo = a)
+        x2 = np.concatenate([a, hi], axis=-1)
+        return np.concatenate([x[:, :(H + 1) // 2], x2[:, (H + 1) // 2:]], axis=1)
+
+    qv, kv = make(w.num_q_heads), make(w.num_kv_heads)
+    ref_q, ref_k = O.rope(qv, opos, w.rope_theta), O.rope(kv, opos, w.rope_theta)
+    # the cancelling outputs really are small next to their inputs
+    m = np.broadcast_to(ok, ref_q[:, :1, :half].shape)
+    assert np.median(np.abs(ref_q[:, :1, :half])[m] / np.abs(qv[:, :1, half:])[m]) < 2.0 ** -6
+    bits = lambda v: f32_to_bf16_bits(v.astype(np.float32))
+    q, k = to_dev(w, bits(qv)), to_dev(w, bits(kv))
+    qr, kr = pg.pg_rope(L, pos, q, k)
+    torch.cuda.synchronize()
+    _rope_compare(w, to_host_f32(qr), ref_q)
+    _rope_compare(w, to_host_f32(kr), ref_k)
 
 
 # --------------------------------------------------------------- attention --
