@@ -463,8 +463,9 @@ struct KvCtx {
   int goff[2];
 };
 
-__device__ inline void kv_fetch(const BwdArgs& a, const KvCtx& c, int n, int stage) {
-  const int m = c.nq - 1 - n / a.r, h = c.hk * a.r + n % a.r;   // query tiles from the top down
+// tile n = (query tile nq - 1 - n / r from the top down, head hk * r + n % r)
+__device__ inline void kv_fetch(const BwdArgs& a, const KvCtx& c, int nt, int nh, int stage) {
+  const int m = c.nq - 1 - nt, h = c.hk * a.r + nh;
   const int q0 = c.q_start + KV_QT * m;
   const int rows = min(KV_QT, c.it->qend - q0);
   const int bytes = (rows - 1) * c.q_row_bytes + D * 2;
@@ -530,7 +531,16 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
   // (dV role), V for dP = dO V^T (dK role)
   // The first tile is fetched while these registers load; the second after
   // their wait, which would otherwise drain it as well.
-  kv_fetch(a, c, 0, 0);
+  // (n / r, n % r) of the next tile to fetch, kept as counters
+  int ft = 0, fh = 0;
+  auto fetch_next = [&](int stage) {
+    kv_fetch(a, c, ft, fh, stage);
+    if (++fh == a.r) {
+      fh = 0;
+      ++ft;
+    }
+  };
+  fetch_next(0);
   bf16x8_t bf[8];
   {
     const bool key_valid = c.key < c.kw1;
@@ -557,16 +567,21 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
   if (c.ntiles > 1) {
-    kv_fetch(a, c, 1, 1);
+    fetch_next(1);
     wait_vmem<KV_LOADS>();
   } else {
     wait_vmem<0>();
   }
   bare_barrier();   // tile 0 has landed
 
+  int lt = 0, lh = 0;   // (n / r, n % r) of this tile
   for (int n = 0; n < c.ntiles; ++n) {
     uint2* const pb = px + (n & 1) * (KV_PBUF / 8);
-    const int q0 = c.q_start + KV_QT * (c.nq - 1 - n / a.r);
+    const int q0 = c.q_start + KV_QT * (c.nq - 1 - lt);
+    if (++lh == a.r) {
+      lh = 0;
+      ++lt;
+    }
     // the slice has keys, and some row of the tile can read one of them
     const bool active = c.wave_keys && q0 + KV_QT - 1 >= c.kw0;
     const unsigned char* st = smem + (n % KV_NSTAGE) * KV_STAGE;
@@ -623,7 +638,16 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
     wait_vmem<0>();
     if constexpr (!KWAVE) wait_lds();
     bare_barrier();
-    if (n + 2 < c.ntiles) kv_fetch(a, c, n + 2, (n + 2) % KV_NSTAGE);
+    // the dK role's P reads go out before the fetch, so that their latency
+    // overlaps its issue
+    uint2 pr[8];
+    if constexpr (KWAVE) {
+      if (active) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) pr[m] = pb[64 * m];
+      }
+    }
+    if (n + 2 < c.ntiles) fetch_next((n + 2) % KV_NSTAGE);
     if (!active) continue;
 
     // second half: dV += P^T dO, or dS = P (dP - D) and dK += dS^T Q (B by
@@ -631,7 +655,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
     if constexpr (KWAVE) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const uint2 p2 = pb[64 * m];
+        const uint2 p2 = pr[m];
         const f16x2_t lo = __builtin_bit_cast(f16x2_t, p2.x);
         const f16x2_t hi = __builtin_bit_cast(f16x2_t, p2.y);
         const float p4[4] = {float(lo.x), float(lo.y), float(hi.x), float(hi.y)};
