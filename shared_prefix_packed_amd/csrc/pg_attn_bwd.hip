@@ -590,8 +590,9 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
     f32x16_t sacc[2];
     if (active) {
       // MFMA blocks run at raised wave priority: the arbiter then favours
-      // whichever wave of the SIMD is feeding the matrix cores
-      __builtin_amdgcn_s_setprio(3);
+      // whichever wave of the SIMD is feeding the matrix cores, the dK role
+      // (the longer of the two per tile) above the dV role
+      __builtin_amdgcn_s_setprio(KWAVE ? 3 : 1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sacc[0][i] = 0.f;
@@ -666,7 +667,7 @@ __device__ inline void kv_loop(const BwdArgs& a, const KvCtx& c, unsigned char* 
       }
     }
     const unsigned char* bt = st + (KWAVE ? 0 : KV_REGION);
-    __builtin_amdgcn_s_setprio(3);
+    __builtin_amdgcn_s_setprio(KWAVE ? 3 : 1);
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       const bf16x8_t pf = pack_step(sacc[s2 >> 1], s2);
