@@ -188,6 +188,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   const int qi = lane & 31;
   const int half = lane >> 5;
 
+  const bool lag = wave >= 4;
   const int h = it.hq0 + wave % a.hpw;
   const int hk = it.hq0 / a.r;
   const int tb = it.t0 + Q_QW * (wave / a.hpw);
@@ -299,12 +300,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
   // behind: first P, dS and the dQ product of the previous tile, then S and dP
   // of this one. The two waves of a SIMD (w and w + 4) thus feed the matrix
   // cores and run the softmax at different times instead of together.
-  const bool lag = wave >= 4;
   f32x16_t sacc[2], pacc[2];
   bool h_part = false, h_full = true;   // second half pending: tile state
   int h_lo = 0, h_hi = 0, h_stage = 0;
 
+  // MFMA blocks at raised wave priority, the lagging waves (whose iteration is
+  // the longer one: both halves meet the other wave's MFMA block) above the
+  // leading ones
   auto first_half = [&](const unsigned char* st) {
+    if (lag) __builtin_amdgcn_s_setprio(3); else __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sacc[0][i] = 0.f;
@@ -329,6 +333,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
         pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], pacc[kb], 0, 0, 0);
       }
     sched_reads_ahead<4, 1, 16>();
+    __builtin_amdgcn_s_setprio(0);
   };
   // P^T and dS^T; register i of block kb holds key ka + 32 kb + 8 (i/4) + 4 half + i%4
   auto second_half = [&](const unsigned char* st, bool full, int lo, int hi) {
@@ -362,6 +367,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) dsf[ks] = pack_step(sacc[ks >> 1], ks);
     // dQ^T += K^T dS^T (K^T by transposing reads of the row-major K tile)
+    if (lag) __builtin_amdgcn_s_setprio(3); else __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -369,6 +375,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs a) {
         dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rowmajor(st, tro, ks, db), dsf[ks],
                                                             dqacc[db], 0, 0, 0);
     sched_reads_ahead<6, 2, 16>();
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Start of iteration n: tile n landed (tile n + 1 may still be in flight);
