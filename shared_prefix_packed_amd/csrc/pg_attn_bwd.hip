@@ -29,8 +29,8 @@
 //    blocks of one segment share that end, so blocks running side by side on
 //    an XCD read the same Q and dO tiles at about the same time. Each 32-key
 //    slice is taken by two waves that share a SIMD, each tile in two halves
-//    split by a workgroup barrier:
-//      dV wave: S = Q K^T, P (to LDS, fp32)  |  dV += P^T dO
+//    split by the tile's workgroup barrier:
+//      dV wave: S = Q K^T, P (to LDS, fp16)  |  dV += P^T dO
 //      dK wave: dP = dO V^T, dP - D          |  dS = P (dP - D), dK += dS^T Q
 //    (A = Q, dO rows from LDS, B = K, V in registers; A = P^T, dS^T from the
 //    accumulators, B = dO, Q by transposing LDS reads; lse and D per query
@@ -40,7 +40,7 @@
 //    registers for the whole block and no atomics are needed.
 // Tiles go HBM -> LDS with buffer loads that write LDS (as in the forward),
 // four (dQ, fetched two tiles ahead) or three (dK, dV) stages deep, with one
-// workgroup barrier per tile (two in dK, dV).
+// workgroup barrier per tile.
 #include <hip/hip_runtime.h>
 
 #include "pg_hip_common.h"
