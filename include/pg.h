@@ -331,7 +331,8 @@ pg_status pg_unpack_rows(const pg_layout* layout, const void* packed, int64_t ro
  *  delta       caller-owned device scratch of Hq * T floats; on return it holds
  *              D = rowsum(dO * O) of every (head, token) row, fp32 [Hq, T]
  * All tensors share dtype. bf16 with d = 128 runs the MFMA kernels (P and dS
- * enter the matrix cores rounded to bf16); fp32, and bf16 with d = 64, run a
+ * enter the matrix cores rounded to bf16; dS is formed from P rounded to fp16,
+ * 11 significant bits); fp32, and bf16 with d = 64, run a
  * reference-grade per-row path (one wave per query row, then one per key row,
  * fp32 arithmetic throughout; for correctness checks and small problems: it
  * reads every query row once per key that the row reads). dq, dk, dv must
