@@ -127,22 +127,6 @@ __device__ inline void sched_reads_ahead() {
   sched_mfma_then_reads<0, NM, PER, NM * PER - AHEAD>();
 }
 
-// fp64 -> bf16 bits, nearest-even, in one rounding (no detour through fp32).
-__device__ inline uint32_t f64_to_bf16_bits(double x) {
-  const uint64_t u = uint64_t(__double_as_longlong(x));
-  const uint64_t mag = u & 0x7fffffffffffffffull;
-  const uint32_t sign = uint32_t(u >> 48) & 0x8000u;
-  if (mag < 0x3810000000000000ull) {   // |x| < 2^-126: below bf16 normals
-    const uint32_t f = __float_as_uint(float(x));   // tiny values go through fp32
-    return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16;
-  }
-  // keep 7 mantissa bits: round at bit 45 of the fp64 pattern, ties to even
-  const uint64_t r = (mag + ((uint64_t(1) << 44) - 1) + ((mag >> 45) & 1)) >> 45;   // exp11|mant7
-  const uint32_t e = uint32_t(r >> 7);                                                // fp64 exponent
-  if (e >= 1023 + 128) return sign | 0x7f80u;                                         // overflow: inf
-  return sign | ((e - 1023 + 127) << 7) | uint32_t(r & 0x7f);
-}
-
 // Rotate-half RoPE of the pair (x_i, x_{i+d/2}) = (xl, xh) by the angle with
 // cosine c and sine s, in fp64 with explicit fused multiply-adds, so every
 // kernel that rotates gets the same bits.

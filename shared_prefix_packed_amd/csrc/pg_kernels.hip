@@ -12,7 +12,6 @@
 
 namespace {
 
-using pg_hip::f64_to_bf16_bits;
 using pg_hip::rope_hi;
 using pg_hip::rope_lo;
 
@@ -57,8 +56,23 @@ struct Vec8<uint16_t> {   // 8 bf16 as raw bits
     const uint32_t w = (&v.x)[e >> 1];
     return double(__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)));
   }
+  // Each value is rounded to fp32 by rounding to odd (truncate, and set the
+  // last bit when anything was cut off), then to bf16 by nearest-even in one
+  // v_cvt_pk_bf16_f32: with 16 bits to spare the two roundings give the
+  // nearest-even bf16 of the fp64 value (Boldo and Melquiond's rounding to
+  // odd), without 64-bit integer arithmetic.
+  __device__ static float to_f32_odd(double d) {
+    const float r = float(d);   // nearest-even
+    const double back = double(r);
+    uint32_t b = __float_as_uint(r);
+    if (back != d) {
+      if (__builtin_fabs(back) > __builtin_fabs(d)) b -= 1u;   // rounded away: truncate
+      b |= 1u;
+    }
+    return __uint_as_float(b);
+  }
   __device__ void set2(int m, double a, double b) {
-    (&v.x)[m] = f64_to_bf16_bits(a) | (f64_to_bf16_bits(b) << 16);
+    (&v.x)[m] = pg_hip::pack_bf16x2(to_f32_odd(a), to_f32_odd(b));
   }
 };
 template <>
