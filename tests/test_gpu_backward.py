@@ -246,7 +246,7 @@ def test_backward_long_prefix_sampled_dq_rows():
     picks = [w.total_tokens - 1]
     for g in range(len(w.prefix_lens)):
         picks += [int(go[g]), int(go[g]) + int(w.prefix_lens[g]) - 1]
-    picks += [int(t) for t in r.integers(0, w.total_tokens, size=16)]
+    picks += [int(t) for t in r.integers(0, w.total_tokens, size=2048)]
     picks += [int(t) for t in np.nonzero(np.diff(np.asarray(lay["ss"])) != 0)[0]]   # last row of each segment
     tokens = sorted(set(picks))
     heads = [int(h) for h in r.integers(0, w.num_q_heads, size=len(tokens))]
@@ -280,12 +280,12 @@ def test_backward_long_prefix_sampled_kv_rows():
     P = int(w.prefix_lens[g])
     rng = np.random.default_rng(405)
     keys = {0, 1, 63, 64, 127, 128, P // 2, P - 65, P - 64, P - 2, P - 1}
-    keys |= {int(t) for t in rng.integers(0, P, size=24)}
+    keys |= {int(t) for t in rng.integers(0, P, size=512)}
     seg = np.asarray(sub["seg_off"])
     for j in range(1, len(seg) - 1):
         s0, s1 = int(seg[j]), int(seg[j + 1])
         if s1 > s0:
-            keys |= {s0, s0 + 1, s1 - 1} | {int(t) for t in rng.integers(s0, s1, size=3)}
+            keys |= {s0, s0 + 1, s1 - 1} | {int(t) for t in rng.integers(s0, s1, size=48)}
     keys = sorted(keys)
     say(f"  {len(keys)} sampled key rows")
     rk, rv, mk, mv = O.attention_backward_kv_rows(q, k, v, do, sub, w.softmax_scale, r, 1, keys,
