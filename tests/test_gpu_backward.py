@@ -295,6 +295,35 @@ def test_backward_long_prefix_sampled_kv_rows():
     compare("dV rows", dv[rows, hk], rv, mv)
 
 
+def test_backward_one_long_group():
+    """One 65.5K-token group (a 60000-token prompt, responses of 3000, 1 and
+    2500 tokens, 8 query heads on one KV head): every dQ, dK, dV element
+    written and finite; sampled dQ rows (prompt and response edges, random)
+    against the oracle's per-row chain rule; over the group's keys dV sums to
+    its dO and dK to zero."""
+    w = make_custom([60000], [[3000, 1, 2500]], num_q_heads=8, num_kv_heads=1, head_dim=128,
+                    dtype="bf16", seed=7)
+    x, dq, dk, dv, L = run_gpu(w)
+    L.close()
+    T = w.total_tokens
+    lay = O.layout(w.prefix_lens, w.suffix_counts, w.suffix_lens)
+    r = np.random.default_rng(707)
+    tokens = {0, 1, 64, 59999, 60000, 62999, 63000, 63001, T - 1}
+    tokens = sorted(tokens | {int(t) for t in r.integers(0, T, size=120)})
+    heads = [int(h) for h in r.integers(0, w.num_q_heads, size=len(tokens))]
+    say(f"backward: one long group, T={T}, {len(tokens)} sampled dQ rows")
+    f = {n: _Bf16Rows(x[n]) for n in ("q", "k", "v", "do")}
+    want, mag = O.attention_backward_dq_rows(f["q"], f["k"], f["v"], f["do"], lay, w.softmax_scale,
+                                             w.num_q_heads, w.num_kv_heads, tokens, heads,
+                                             magnitudes=True)
+    compare("dQ rows", dq[tokens, heads], want, mag)
+    assert np.isfinite(dk).all() and np.isfinite(dv).all()
+    do = bf16_bits_to_f32(x["do"]).astype(np.float64)
+    want_v = do.sum(axis=(0, 1))
+    assert np.abs(dv[:, 0].sum(axis=0) - want_v).max() <= 1e-2 * max(1.0, np.abs(want_v).max()) + 0.5
+    assert np.abs(dk[:, 0].sum(axis=0)).max() <= 1e-2 * np.abs(dk[:, 0]).sum(axis=0).max() + 1e-3
+
+
 def test_backward_deterministic_and_fully_written():
     w = make_workload(1)
     x = {n: draw_tensor(w, n) for n in ("q", "k", "v", "do")}

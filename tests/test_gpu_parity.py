@@ -262,6 +262,36 @@ def test_pipeline_against_oracle(i):
     check_attn(w, o, lse, q_ref, k_ref, vh, lay, full=parity_mode(i))
 
 
+def test_attention_one_long_group():
+    """One group far longer than any workload's: a 60000-token prompt and three
+    responses (3000, 1 and 2500 tokens), 8 query heads on one KV head, so one
+    (group, KV head) cluster spans about a thousand work items and a response
+    row's prompt span about 940 key tiles. Every output is written (NaN
+    poison); sampled rows (both ends of the prompt and of every response,
+    64-token block edges, random) against the oracle's per-row definition."""
+    w = make_custom([60000], [[3000, 1, 2500]], num_q_heads=8, num_kv_heads=1, seed=7)
+    x = draw_qkv(w)
+    L = layout_of(w)
+    q, k, v = (to_dev(w, x[n]) for n in ("q", "k", "v"))
+    o, lse = poisoned_outputs(q, w.num_q_heads)
+    pg.pg_attn_fwd(L, q, k, v, w.softmax_scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    o_g, l_g = to_host_f32(o), lse.cpu().numpy()
+    assert np.isfinite(o_g).all() and np.isfinite(l_g).all()
+    T = w.total_tokens
+    r = np.random.default_rng(17)
+    tokens = {0, 1, 63, 64, 30000, 59999, 60000, 60001, 62999, 63000, 63001, 63002, T - 1}
+    tokens = sorted(tokens | {int(t) for t in r.integers(0, T, size=240)})
+    heads = [int(h) for h in r.integers(0, w.num_q_heads, size=len(tokens))]
+    qh, kh, vh = (host_vals(w, x[n]) for n in ("q", "k", "v"))
+    ro, rl = O.attention_rows(qh, kh, vh, oracle_layout(w), w.softmax_scale, w.num_q_heads,
+                              w.num_kv_heads, tokens, heads)
+    eo = np.abs(o_g[tokens, heads].astype(np.float64) - ro).max()
+    el = np.abs(l_g[heads, tokens].astype(np.float64) - rl).max()
+    say(f"  one long group (T={T}): {len(tokens)} sampled rows: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= O_TOL and el <= LSE_TOL
+
+
 EDGE = [
     # prefix lens, suffix lens, (Hq, Hkv), d
     ([0, 7], [[4, 3], [5]], (4, 1), 128),

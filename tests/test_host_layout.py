@@ -219,6 +219,7 @@ def _status(fn, *args):
     (([5], [1], [3], 4, 1, 96, 1e4), -2),         # unsupported head_dim
     (([5], [1], [3], 4, 1, 128, 0.0), -1),        # theta
     (([2**30, 2**30], [0, 0], [], 4, 1, 128, 1e4), -1),   # T >= 2^31
+    (([2**30 - 1], [1], [2], 4, 1, 128, 1e4), -1),        # T = 2^30 + 1: one past the limit
 ])
 def test_invalid_arguments_are_reported(args, status):
     assert _status(pg.pg_build_layout_host, *args) == status
