@@ -362,8 +362,8 @@ def main(argv=None):
     ap.add_argument("--profile-summary", action="store_true",
                     help="no GPU work: write the --workload's profile summary (markdown, stdout) from "
                          "the output of the --profile-recipe runs")
-    ap.add_argument("--profile-dir", default="gpurun_out/prof",
-                    help="where the --profile-recipe runs write (default gpurun_out/prof)")
+    ap.add_argument("--profile-dir", default="rocprof_out",
+                    help="where the --profile-recipe runs write (default rocprof_out)")
     ap.add_argument("--record-traffic", action="store_true",
                     help="with --profile-summary: store the attention launch's calibrated HBM bytes in "
                          "profiles/attn_traffic.json under the current kernel source hash")

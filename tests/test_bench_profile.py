@@ -95,8 +95,8 @@ def test_profile_summary_figures(tmp_path, monkeypatch, capsys):
 
 
 def test_profile_recipe_names_committed_programs_only():
-    for _, out, cmd in bench.profile_recipe(2, "gpurun_out/prof"):
-        assert out.startswith("gpurun_out/prof/")
+    for _, out, cmd in bench.profile_recipe(2, "rocprof_out"):
+        assert out.startswith("rocprof_out/")
         assert "-- python3 bench.py" in cmd
         assert cmd.startswith("timeout -s KILL ")
         assert "cd " not in cmd
