@@ -10,7 +10,8 @@
 // row once, with enough bytes in flight to keep HBM busy:
 //
 //  * decode_partial_kernel: one wave per work item (host-built, launch order,
-//    XCD-balanced): up to 512 cache rows of one KV head inside one segment, for
+//    XCD-balanced): up to 512 cache rows (1024 in a prompt longer than 4096
+//    rows) of one KV head inside one segment, for
 //    up to 32 query rows (the responses of a group for a prompt chunk, one
 //    response for a response chunk). Inside an item every query row sees every
 //    key, so there is no per-row mask; a response chunk stops at the

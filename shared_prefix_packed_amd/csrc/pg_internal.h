@@ -154,5 +154,7 @@ constexpr int PG_KEY_TILE = 64;       // keys per LDS tile
 constexpr int PG_XCDS = 8;            // XCDs of an MI355X; workgroup p runs on XCD p % 8
 constexpr int PG_KV_BLOCK = 128;      // keys per backward dK/dV work item (4 waves x 32)
 constexpr int PG_DEC_CHUNK = 512;     // most cache rows per decode work item
+constexpr int PG_DEC_LONG_PROMPT = 4096;  // prompts longer than this are chunked by
+constexpr int PG_DEC_CHUNK_LONG = 1024;   // up to this many rows per work item
 constexpr int PG_DEC_TARGET = 1024;   // decode work items aimed at per step
 constexpr int PG_DEC_ROWS = 32;       // most query rows per decode work item (one MFMA column block)

@@ -351,10 +351,15 @@ pg_status pg_layout_build_host(pg_layout& L, int32_t num_groups, const int32_t* 
       const int32_t chunk =
           int32_t(std::min<int64_t>(PG_DEC_CHUNK, std::max<int64_t>(64, (per_item + 31) / 32 * 32)));
       L.dec_chunk = chunk;
+      // A prompt much longer than a chunk is cut into fewer, longer pieces:
+      // every piece of it already has enough rows to stream, and each extra
+      // piece adds a partial result to write and merge and a work item to
+      // start (a 16K-row prompt: 14 % faster steps with 1024-row pieces).
       auto chunked = [&](int32_t a, int32_t b, int32_t resp, int32_t rows0, int32_t nrows) {
         if (b <= a || nrows <= 0) return;
         const int32_t len = b - a;
-        const int32_t nch = (len + chunk - 1) / chunk;
+        const int32_t ck = (resp < 0 && len > PG_DEC_LONG_PROMPT) ? PG_DEC_CHUNK_LONG : chunk;
+        const int32_t nch = (len + ck - 1) / ck;
         const int32_t step = ((len + nch - 1) / nch + 31) / 32 * 32;
         for (int32_t k0 = a; k0 < b; k0 += step) {
           const int32_t k1 = std::min(b, k0 + step);

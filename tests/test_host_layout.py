@@ -353,7 +353,9 @@ def _check_decode_invariants(L, P, S, hq, hkv, d=128):
             assert (k0, k1, hk, resp, seg0, seg1, row0) == (0, 0, 0, -1, 0, 0, 0)
             continue
         assert 1 <= nrow <= 32 and 0 <= hk < hkv
-        assert seg0 <= k0 < k1 <= seg1 and k1 - k0 <= 512 and (k0 - seg0) % 32 == 0
+        # pieces of at most 512 rows; of a prompt longer than 4096 rows, 1024
+        most = 1024 if (resp < 0 and seg1 - seg0 > 4096) else 512
+        assert seg0 <= k0 < k1 <= seg1 and k1 - k0 <= most and (k0 - seg0) % 32 == 0
         if resp < 0:
             g = int(np.searchsorted(group_off, seg0, side="right") - 1)
             assert seg0 == group_off[g] and seg1 == group_off[g] + P[g]
@@ -407,6 +409,22 @@ def test_decode_work_list_on_long_segments():
         assert all(x == sizes[0] and x % 32 == 0 for x in sizes[:-1]) and sizes[-1] <= sizes[0]
     # the chunk length aims at about 1024 items: 2855 rows x 2 KV heads -> 64
     assert int((real["k1"] - real["k0"]).max()) == 64
+
+
+def test_decode_work_list_long_prompt_pieces():
+    # a prompt longer than 4096 rows is cut into pieces of up to 1024 rows
+    # (10000 rows: ten balanced pieces of 1024, the last 784); its responses
+    # keep the ordinary chunk length
+    P, S = [10000], [[300, 700]]
+    L = _build(P, S, hq=8, hkv=2)
+    _check_decode_invariants(L, P, S, 8, 2)
+    items, _, _ = L.decode_work()
+    real = items[(items["nrow"] > 0) & (items["hk"] == 0)]
+    prompt = real[real["resp"] < 0]
+    sizes = sorted(set((prompt["k1"] - prompt["k0"]).tolist()))
+    assert sizes == [784, 1024]
+    resp = real[real["resp"] >= 0]
+    assert int((resp["k1"] - resp["k0"]).max()) <= 512
 
 
 def test_decode_work_list_on_dpo_workload():
