@@ -108,6 +108,7 @@ EDGE = [
     ([1500], [[50, 1100]], 32, 1, [-3, 4000]),                    # clamping, r = 32: 64 rows
     ([0, 0], [[0], []], 4, 4, [5]),                               # no tokens at all
     ([100, 0, 37], [[], [17, 0], [1, 1, 1]], 2, 2, [17, 0, 1, 0, 1]),
+    ([4097, 40], [[100, 2000], [7]], 8, 2, None),                 # prompt past 4096 rows: longer pieces
 ]
 
 
